@@ -1,0 +1,141 @@
+/*
+ * ncc.h -- C ABI of libncc.so: normalized cross-correlation (NCC) template
+ * matching of 8-bit images, with window sums from summed-area tables, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow The CUDA Handbook, chapter 15:
+ *   - "Image in shared memory": the per-window accumulation of SumI, SumISq
+ *     and SumIT over a wT x hT template (corrShared_kernel listing) and the
+ *     coefficient computed from them (CorrelationValue, whose body the page
+ *     does not print; this library uses the textbook Pearson coefficient,
+ *     stated at ncc_correlate below).
+ *   - Section 15.8 "The Denominator: Summed Area Tables": the inclusive
+ *     summed-area table of I and of I^2 (int64, uint32 row running sums,
+ *     built as a row scan then a column scan) and the four-corner satBox
+ *     query with the table's two leading edges read as zero.
+ *
+ * Conventions for every entry point:
+ *   - Images are H rows x W columns of uint8, row-major, dense (pitch = W).
+ *   - Buffer arguments are DEVICE pointers (memory from hipMalloc or from a
+ *     framework allocator on the current device).  The caller allocates and
+ *     owns them; the library never frees or keeps them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns without waiting for it.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call launches nothing and leaves every output untouched.
+ *   - Return value: NCC_OK or a negative NCC_E* code (ncc_strerror names it).
+ *   - The library keeps a per-device, per-stream workspace cache (growing,
+ *     freed by ncc_release).  Calls on one stream are ordered by the stream;
+ *     calls on different streams use different workspaces.
+ */
+#ifndef NCC_H
+#define NCC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NCC_OK 0
+#define NCC_EINVAL (-1)        /* null pointer, size < 1, template larger than image ... */
+#define NCC_ERANGE (-2)        /* sizes past the integer widths the method relies on */
+#define NCC_ENOMEM (-3)        /* workspace allocation failed */
+#define NCC_EHIP (-4)          /* a HIP runtime call or kernel launch failed */
+#define NCC_EUNSUPPORTED (-5)  /* shape this build has no kernel for (see ncc_correlate) */
+
+/* Largest image width: one row's running sum of squares, at most W*255^2,
+ * must fit the uint32 row partials of the table build (section 15.8 width
+ * analysis): W*65025 <= 2^32 - 1. */
+#define NCC_MAX_WIDTH 66051
+/* Largest template pixel count: SumISq <= K*255^2 and SumIT <= K*255^2 must
+ * fit the int32 sums of the window loop (corrShared_kernel accumulates in
+ * int): K*65025 <= 2^31 - 1. */
+#define NCC_MAX_TEMPLATE_PIXELS 33025
+
+/*
+ * ncc_sat_build -- summed-area tables of an image (section 15.8: table
+ * definition, width analysis, row-scan-then-column-scan build).
+ *
+ *   img  [H][W] uint8, device.
+ *   S    [H][W] int64, device, written: S(x,y) = sum of I over rows 0..y and
+ *        columns 0..x (inclusive).
+ *   Q    [H][W] int64, device, written: the same sum of I^2.
+ *
+ * Errors: NCC_EINVAL (null pointer, W < 1, H < 1), NCC_ERANGE (W >
+ * NCC_MAX_WIDTH, or W*H*65025 past int64), NCC_ENOMEM, NCC_EHIP.
+ */
+int ncc_sat_build(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q,
+                  void *stream);
+
+/*
+ * ncc_box -- batched four-corner box sums on one table (section 15.8:
+ * four-corner equation and satBox listing).
+ *
+ *   S      [H][W] int64 table from ncc_sat_build (S or Q), device.
+ *   rects  [n][4] int32 {x0, y0, x1, y1}, device: the half-open box
+ *          [x0,x1) x [y0,y1).
+ *   out    [n] int64, device, written: D - B - C + A, with corners outside
+ *          the table's leading edges read as zero.  An empty box
+ *          (x0 == x1 or y0 == y1) gives 0.  A box outside
+ *          0 <= x0 <= x1 <= W, 0 <= y0 <= y1 <= H gives INT64_MIN (the
+ *          check runs on the device; there is no error return for it).
+ *   n      number of boxes; n == 0 launches nothing and returns NCC_OK.
+ *
+ * Errors: NCC_EINVAL (null pointer with n > 0, W < 1, H < 1, n < 0),
+ * NCC_EHIP.
+ */
+int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n,
+            int64_t *out, void *stream);
+
+/*
+ * ncc_correlate -- valid-mode normalized cross-correlation of an image with
+ * one template or a bank of templates ("Image in shared memory":
+ * corrShared_kernel's window sums; section 15.8: window sums from the tables
+ * by the four-corner rule).
+ *
+ *   img       [H][W] uint8, device.
+ *   tpl       [nTpl][hT][wT] uint8, device.
+ *   sums_out  nullable; [(2+nTpl)][Ho][Wo] int32, device: plane 0 SumI,
+ *             plane 1 SumISq, plane 2+t SumIT of template t, with
+ *             Wo = W-wT+1, Ho = H-hT+1.  Position (x,y) covers rows
+ *             y..y+hT-1 and columns x..x+wT-1.
+ *   coef_out  [nTpl][Ho][Wo] float32, device:
+ *               num  = K*SumIT - SumI*SumT,   K = wT*hT
+ *               varI = K*SumISq - SumI^2,     varT = K*SumTSq - SumT^2
+ *               gamma = num / sqrt(varI*varT), and 0 when varI or varT is 0.
+ *             num, varI and varT are exact integers; the float evaluation
+ *             after them is within 1e-5 of the correctly rounded value.
+ *
+ * Window sums SumI and SumISq are exact integers taken from summed-area
+ * tables of the image by the four-corner rule (tables of each on-chip image
+ * strip for the specialised kernels, the full int64 tables of ncc_sat_build
+ * in the workspace otherwise).  A bank (nTpl > 1) of templates with at most
+ * 16 rows of at most 16 pixels runs SumIT as an int8 matrix-core
+ * contraction; other shapes run per template on the vector units.
+ *
+ * Errors: NCC_EINVAL (null img/tpl/coef_out, W or H < 1, wT or hT < 1,
+ * wT > W, hT > H, nTpl < 1), NCC_ERANGE (W > NCC_MAX_WIDTH,
+ * wT*hT > NCC_MAX_TEMPLATE_PIXELS, outputs past 2^62 bytes),
+ * NCC_EUNSUPPORTED (a template whose staged image tile does not fit the
+ * 160 KiB of LDS of one workgroup), NCC_ENOMEM, NCC_EHIP.
+ */
+int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl,
+                  int wT, int hT, int nTpl, int32_t *sums_out,
+                  float *coef_out, void *stream);
+
+/* Static string naming a status code. */
+const char *ncc_strerror(int status);
+
+/* Frees every cached workspace on every device.  Waits for the streams that
+ * used them.  Later calls allocate again. */
+void ncc_release(void);
+
+/* ABI version of this header (major*100 + minor). */
+int ncc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NCC_H */

@@ -1,0 +1,166 @@
+"""Python binding of libncc.so: NCC template matching with summed-area tables
+on MI355X (gfx950).
+
+This module only marshals torch tensors (device memory and streams) into the C
+ABI declared in ``include/ncc.h``; every step of the computation runs in the
+library's HIP kernels.  The library must be built (``python -m
+normalized_cross_correlation_amd.build``); without it every call raises.
+
+Functions take and return torch tensors on a ROCm device and enqueue work on
+the tensor device's current torch stream:
+
+* ``sat_build(img)``             -> (S, Q) int64 summed-area tables
+* ``box(S, rects)``              -> int64 four-corner box sums
+* ``correlate(img, tpl, sums)``  -> (coef float32 [n][Ho][Wo], sums int32 or None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["sat_build", "box", "correlate", "release", "lib", "NCCError",
+           "ABI_FUNCTIONS", "LIB_PATH", "MAX_WIDTH", "MAX_TEMPLATE_PIXELS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libncc.so")
+ABI_FUNCTIONS = ("ncc_sat_build", "ncc_box", "ncc_correlate", "ncc_strerror",
+                 "ncc_release", "ncc_version")
+MAX_WIDTH = 66051
+MAX_TEMPLATE_PIXELS = 33025
+
+_lib = None
+
+
+class NCCError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__("%s failed: %s (%d)" % (fn, msg, code))
+        self.code = code
+
+
+def lib():
+    """The loaded libncc.so (ctypes), with argument types set."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (loads torch's HIP runtime first; libncc shares it)
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libncc.so is not built: run `python -m "
+                               "normalized_cross_correlation_amd.build` (%s)" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.ncc_sat_build.argtypes = [P, I, I, P, P, P]
+        L.ncc_sat_build.restype = I
+        L.ncc_box.argtypes = [P, I, I, P, I64, P, P]
+        L.ncc_box.restype = I
+        L.ncc_correlate.argtypes = [P, I, I, P, I, I, I, P, P, P]
+        L.ncc_correlate.restype = I
+        L.ncc_strerror.argtypes = [I]
+        L.ncc_strerror.restype = ctypes.c_char_p
+        L.ncc_release.argtypes = []
+        L.ncc_release.restype = None
+        L.ncc_version.argtypes = []
+        L.ncc_version.restype = I
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise NCCError(fn, rc, lib().ncc_strerror(rc).decode())
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev_tensor(t, dtype, name, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a ROCm device" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions" % (name, ndim))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def sat_build(img, S=None, Q=None):
+    """Summed-area tables of a [H][W] uint8 image: S of I and Q of I^2 (int64,
+    inclusive).  Pass S, Q to write into existing tensors."""
+    import torch
+    _dev_tensor(img, torch.uint8, "img", 2)
+    H, W = img.shape
+    if S is None:
+        S = torch.empty((H, W), dtype=torch.int64, device=img.device)
+    if Q is None:
+        Q = torch.empty((H, W), dtype=torch.int64, device=img.device)
+    for name, t in (("S", S), ("Q", Q)):
+        _dev_tensor(t, torch.int64, name, 2)
+        if tuple(t.shape) != (H, W) or t.device != img.device:
+            raise ValueError("%s must be [H][W] on the image's device" % name)
+    with torch.cuda.device(img.device):
+        _check("ncc_sat_build", lib().ncc_sat_build(
+            img.data_ptr(), W, H, S.data_ptr(), Q.data_ptr(), _stream(img)))
+    return S, Q
+
+
+def box(S, rects, out=None):
+    """Four-corner box sums of one table S for rects [n][4] int32 {x0,y0,x1,y1}.
+    Boxes outside the table give INT64_MIN, empty boxes 0."""
+    import torch
+    _dev_tensor(S, torch.int64, "S", 2)
+    _dev_tensor(rects, torch.int32, "rects", 2)
+    if rects.shape[1] != 4:
+        raise ValueError("rects must be [n][4]")
+    H, W = S.shape
+    n = rects.shape[0]
+    if out is None:
+        out = torch.empty((n,), dtype=torch.int64, device=S.device)
+    _dev_tensor(out, torch.int64, "out", 1)
+    if out.shape[0] != n:
+        raise ValueError("out must have n elements")
+    with torch.cuda.device(S.device):
+        _check("ncc_box", lib().ncc_box(S.data_ptr(), W, H, rects.data_ptr(), n,
+                                        out.data_ptr(), _stream(S)))
+    return out
+
+
+def correlate(img, tpl, want_sums: bool = False, coef=None, sums=None):
+    """Valid-mode NCC of a [H][W] uint8 image with a [hT][wT] template or a
+    [n][hT][wT] bank.  Returns (coef float32 [n][Ho][Wo], sums int32
+    [2+n][Ho][Wo] or None): sums planes are SumI, SumISq, then SumIT per
+    template."""
+    import torch
+    _dev_tensor(img, torch.uint8, "img", 2)
+    if tpl.dim() == 2:
+        tpl = tpl.unsqueeze(0)
+    _dev_tensor(tpl, torch.uint8, "tpl", 3)
+    H, W = img.shape
+    n, hT, wT = tpl.shape
+    Ho, Wo = H - hT + 1, W - wT + 1
+    if Ho < 1 or Wo < 1:
+        raise ValueError("template larger than the image")
+    if coef is None:
+        coef = torch.empty((n, Ho, Wo), dtype=torch.float32, device=img.device)
+    _dev_tensor(coef, torch.float32, "coef", 3)
+    if tuple(coef.shape) != (n, Ho, Wo):
+        raise ValueError("coef must be [n][Ho][Wo]")
+    if want_sums and sums is None:
+        sums = torch.empty((2 + n, Ho, Wo), dtype=torch.int32, device=img.device)
+    if sums is not None:
+        _dev_tensor(sums, torch.int32, "sums", 3)
+        if tuple(sums.shape) != (2 + n, Ho, Wo):
+            raise ValueError("sums must be [2+n][Ho][Wo]")
+    with torch.cuda.device(img.device):
+        _check("ncc_correlate", lib().ncc_correlate(
+            img.data_ptr(), W, H, tpl.data_ptr(), wT, hT, n,
+            sums.data_ptr() if sums is not None else None, coef.data_ptr(), _stream(img)))
+    return coef, sums
+
+
+def release():
+    """Frees the library's cached workspaces."""
+    lib().ncc_release()

@@ -1,0 +1,160 @@
+// Internal declarations shared by the HIP sources of libncc.so.
+// Written for gfx950 (CDNA4): 64-lane wavefronts, DPP row operations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace ncc {
+
+// ---------------------------------------------------------------- tables ---
+// Table build tiling: a workgroup of 4 wavefronts owns a tile of
+// SAT_SW columns x SAT_BH rows; each lane owns 4 adjacent columns and each
+// wavefront 16 rows of the tile.
+constexpr int SAT_SW = 256;
+constexpr int SAT_BH = 64;
+
+struct SatWork {
+    int nStrips, nBands;
+    uint32_t *colsum;   // [2][nBands][W]    column sums of each band
+    uint32_t *rowtot;   // [2][H][nStrips]   row sums of each strip
+    uint64_t *tiletot;  // [2][nBands][nStrips]
+    uint64_t *cp;       // [2][nBands][W]    column sums of all rows above the band
+    uint32_t *lrow;     // [2][H][nStrips]   row sums of all columns left of the strip
+    int64_t *corner;    // [2][nBands][nStrips] table value above-left of the tile
+};
+
+size_t sat_work_bytes(int W, int H);
+SatWork sat_work_carve(void *base, int W, int H);
+hipError_t sat_build_launch(const uint8_t *img, int W, int H, int64_t *S,
+                            int64_t *Q, const SatWork &wk, hipStream_t st);
+
+hipError_t box_launch(const int64_t *S, int W, int H, const int32_t *rects,
+                      int64_t n, int64_t *out, hipStream_t st);
+
+// ------------------------------------------------------------- templates ---
+// Per-template constants computed on the device.
+struct TStat {
+    long long sumT;    // sum of T
+    long long sumTSq;  // sum of T^2
+    long long varT;    // K*sumTSq - sumT^2 (exact)
+    float varTf;       // (float)varT
+    float rT;          // 1/sqrt(varT), 0 when varT == 0
+};
+
+// Packed forms of a template bank written by tpl_prep_launch:
+//  rows: [nTpl][hT][WT4] uint32, each template row zero-padded to WT4 = ceil(wT/4)
+//        dwords (little-endian bytes).
+//  mfma: for banks eligible for the matrix-core kernel,
+//        [nGroups of 16 templates][KSTEPS][64 lanes][16 bytes] int8 with
+//        T' = T - 128; chunk c = 4*kstep + lane/16 is template row c / NB16,
+//        bytes 16*(c % NB16) .. +15 (NB16 = ceil(wT/16)); padding is 0.
+size_t tpl_rows_bytes(int wT, int hT, int nTpl);
+size_t tpl_mfma_bytes(int wT, int hT, int nTpl);
+hipError_t tpl_prep_launch(const uint8_t *tpl, int wT, int hT, int nTpl,
+                           uint32_t *rows, int8_t *mfma, TStat *stats,
+                           hipStream_t st);
+
+// ----------------------------------------------------------- correlation ---
+struct CorrArgs {
+    const uint8_t *img;
+    const uint8_t *tpl;    // [nTpl][hT][wT] as given by the caller
+    int W, H, wT, hT, nTpl, Wo, Ho;
+    const uint32_t *rows;  // packed template rows
+    const int8_t *mfma;    // packed bank operands (bank kernel only)
+    const TStat *stats;
+    int32_t *sums;         // nullable
+    float *coef;
+};
+
+// Specialised single-template kernels (an on-chip table of each image strip
+// supplies SumI / SumISq).  Returns hipErrorNotSupported when no kernel fits
+// the shape.
+bool corr_stream_supported(int wT, int hT);
+hipError_t corr_stream_launch(const CorrArgs &a, int t, hipStream_t st);
+
+// Any shape: window sums from the full int64 tables S, Q.
+bool corr_generic_supported(int wT, int hT);
+hipError_t corr_generic_launch(const CorrArgs &a, int t, const int64_t *S,
+                               const int64_t *Q, hipStream_t st);
+
+// Template bank on the int8 matrix cores.
+bool corr_bank_supported(int wT, int hT, int nTpl);
+hipError_t corr_bank_launch(const CorrArgs &a, hipStream_t st);
+
+// ---------------------------------------------------- device utilities ---
+#ifdef __HIP_DEVICE_COMPILE__
+#define NCC_DEV __device__ __forceinline__
+#else
+#define NCC_DEV __device__ inline
+#endif
+
+// DPP control codes (GFX9 encoding).
+constexpr int DPP_ROW_SHR1 = 0x111;
+constexpr int DPP_ROW_SHR2 = 0x112;
+constexpr int DPP_ROW_SHR4 = 0x114;
+constexpr int DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142;
+constexpr int DPP_ROW_BCAST31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (Hillis-Steele on
+// DPP: shifts within 16-lane rows, then the two row broadcasts).
+NCC_DEV uint32_t wave_incl_scan_u32(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, DPP_ROW_SHR1, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, DPP_ROW_SHR2, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, DPP_ROW_SHR4, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, DPP_ROW_SHR8, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, DPP_ROW_BCAST15, 0xa, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, DPP_ROW_BCAST31, 0xc, 0xf, false);
+    return x;
+}
+
+template <int CTRL, int ROWMASK>
+NCC_DEV uint64_t dpp_u64(uint64_t v) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, ROWMASK, 0xf, false);
+    hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, ROWMASK, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+NCC_DEV uint64_t wave_incl_scan_u64(uint64_t x) {
+    x += dpp_u64<DPP_ROW_SHR1, 0xf>(x);
+    x += dpp_u64<DPP_ROW_SHR2, 0xf>(x);
+    x += dpp_u64<DPP_ROW_SHR4, 0xf>(x);
+    x += dpp_u64<DPP_ROW_SHR8, 0xf>(x);
+    x += dpp_u64<DPP_ROW_BCAST15, 0xa>(x);
+    x += dpp_u64<DPP_ROW_BCAST31, 0xc>(x);
+    return x;
+}
+
+// Sum over the wavefront, returned in every lane (uniform).
+NCC_DEV uint32_t wave_sum_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_u32(x), 63);
+}
+
+NCC_DEV uint32_t dot4u(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_udot4(a, b, c, false);
+}
+
+// Bytes s .. s+3 of the 8-byte little-endian value hi:lo (s in 0..3).
+NCC_DEV uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t s) {
+    return __builtin_amdgcn_alignbyte(hi, lo, s);
+}
+
+// Mask keeping the low nb bytes of a dword (nb in 1..4).
+NCC_DEV uint32_t byte_mask(int nb) {
+    return nb >= 4 ? 0xffffffffu : ((1u << (8 * nb)) - 1u);
+}
+
+// The coefficient from exact integer numerator and window variance and the
+// template's variance as float.  A zero variance yields 0: varI == 0 forces
+// num == 0 (every window pixel equal), varT == 0 likewise, so clamping the
+// product to >= 1 only guards 0 * inf.
+NCC_DEV float ncc_coef(float numf, float varIf, float varTf) {
+    float p = fmaxf(varIf * varTf, 1.0f);
+    float g = numf * __builtin_amdgcn_rsqf(p);
+    return __builtin_amdgcn_fmed3f(g, -1.0f, 1.0f);
+}
+
+}  // namespace ncc
