@@ -1,0 +1,274 @@
+"""Benchmark of the NCC hot path on one MI355X.
+
+Step (the timed unit): on the headline workload -- a 4096 x 4096 uint8
+smooth-noise image and one 16 x 16 template cut from it -- build both
+summed-area tables (ncc_sat_build: S and Q, int64) and correlate
+(ncc_correlate: 4081 x 4081 valid-mode float32 coefficients).  Inputs are
+resident in device memory before timing starts.
+
+Printed: ONE JSON line.  `value` is coefficients per second of whole steps
+(Gcoeff/s).  `roofline` covers the step's dominant kernel, timed with HIP
+events around its calls inside the timed region.  Also reported, from the same
+run: the table build alone on 4096 x 4096 uniform bytes (GB/s of algorithmic
+traffic, 17 B per pixel) with 1 000 000 box queries, and the 64-template bank
+workload; and the CPU oracle timed on a bounded sample (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+HBM_PEAK_GBS = 8000.0
+CUS, CLOCK_GHZ = 256, 2.4
+# v_dot4_u32_u8: 4 u8 multiply-accumulates per lane per instruction, one
+# wavefront instruction per 4 clocks per SIMD (16 lanes/clock), 4 SIMDs per CU
+# -> 256 CUs * 64 lanes * 4 MAC * 2.4 GHz = 157.3 TMAC/s = 314.6 TOP/s
+DOT4_PEAK_TOPS = CUS * 64 * 4 * 2 * CLOCK_GHZ / 1000.0
+INT8_MFMA_PEAK_TOPS = 5000.0
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "normalized_cross_correlation_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_names):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("src_hash") != _src_hash(*src_names):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_calls(fns, steps, warmup, stream):
+    """Runs `steps` steps of the callables in `fns` (one step = each once, in
+    order) after `warmup` untimed steps.  Returns (wall seconds of the timed
+    steps, mean ms of each callable from HIP events on `stream`)."""
+    import torch
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+           for i in range(len(fns))]
+    return wall, per
+
+
+def cpu_baseline(img, tpl, budget_s=12.0):
+    """The oracle (plain C, OpenMP over output rows) on the first R output rows
+    of the headline image, R sized so the run takes about budget_s."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.threads(0)
+    hT, wT = tpl.shape[-2:]
+    Wo = img.shape[1] - wT + 1
+
+    def run(rows):
+        sub = np.ascontiguousarray(img[: rows + hT - 1])
+        t0 = time.perf_counter()
+        oracle.correlate(sub, tpl, want_sums=False)
+        return time.perf_counter() - t0
+
+    probe_rows = 16
+    tp = run(probe_rows)
+    rows = int(max(probe_rows, min(img.shape[0] - hT + 1, probe_rows * budget_s / max(tp, 1e-6))))
+    t = run(rows)
+    coeffs = rows * Wo
+    return {
+        "value": round(coeffs / t / 1e9, 6),
+        "unit": "Gcoeff/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "oracle_correlate (its own table build + per-window loops, int64/double) on the "
+                  "first %d output rows x %d columns of the headline 4096x4096 image, 16x16 "
+                  "template: %d coefficients in %.2f s on %d threads" % (rows, Wo, coeffs, t, threads),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the headline step (used under the profiler)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import normalized_cross_correlation_amd as ncc
+    from normalized_cross_correlation_amd import synth
+
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    stream = torch.cuda.current_stream(d)
+    L = ncc.lib()
+    sh = stream.cuda_stream
+
+    # ---------------------------------------------------------- headline --
+    w = synth.make("headline")
+    img_np, tpl_np = w["img"], w["tpl"]
+    H, W = img_np.shape
+    _, hT, wT = tpl_np.shape
+    Ho, Wo = H - hT + 1, W - wT + 1
+    img = torch.from_numpy(img_np).to(d)
+    tpl = torch.from_numpy(tpl_np).to(d)
+    S = torch.empty((H, W), dtype=torch.int64, device=d)
+    Q = torch.empty((H, W), dtype=torch.int64, device=d)
+    coef = torch.empty((1, Ho, Wo), dtype=torch.float32, device=d)
+    pi, pt, pS, pQ, pc = img.data_ptr(), tpl.data_ptr(), S.data_ptr(), Q.data_ptr(), coef.data_ptr()
+
+    def sat():
+        rc = L.ncc_sat_build(pi, W, H, pS, pQ, sh)
+        if rc:
+            raise RuntimeError("ncc_sat_build: %d" % rc)
+
+    def corr():
+        rc = L.ncc_correlate(pi, W, H, pt, wT, hT, 1, None, pc, sh)
+        if rc:
+            raise RuntimeError("ncc_correlate: %d" % rc)
+
+    wall, (t_sat, t_corr) = time_calls([sat, corr], args.steps, args.warmup, stream)
+    ms_step = wall / args.steps * 1e3
+    coeffs = Ho * Wo
+    value = coeffs / (ms_step * 1e-3) / 1e9
+
+    # correctness guard on what was timed: coefficient 1 at the cut
+    (cx, cy), = w["cut_xy"]
+    assert abs(float(coef[0, cy, cx]) - 1.0) <= 1e-5
+
+    sat_bytes = H * W * 17  # read u8 once, write two int64 tables once
+    corr_ops = coeffs * hT * wT * 2  # u8 multiply-accumulates, 2 ops each
+    sat_rate = sat_bytes / (t_sat * 1e-3) / 1e9
+    corr_rate = corr_ops / (t_corr * 1e-3) / 1e12
+    comp = {
+        "ncc_sat_build": {"ms": round(t_sat, 5), "GB/s": round(sat_rate, 1),
+                          "frac_hbm": round(sat_rate / HBM_PEAK_GBS, 4),
+                          "kernels": "sat_reduce, sat_carry, sat_downsweep"},
+        "ncc_correlate": {"ms": round(t_corr, 5), "Gcoeff/s": round(coeffs / (t_corr * 1e-3) / 1e9, 1),
+                          "TOP/s": round(corr_rate, 2), "frac_dot4": round(corr_rate / DOT4_PEAK_TOPS, 4),
+                          "kernels": "corr_stream<4,16>"},
+    }
+    if t_corr >= t_sat:
+        roof = {"kernel": "corr_stream<4,16> (ncc_correlate, one launch)", "bound": "alu",
+                "achieved": round(corr_rate, 2), "peak": round(DOT4_PEAK_TOPS, 1), "unit": "TOP/s",
+                "frac": round(corr_rate / DOT4_PEAK_TOPS, 4),
+                "traffic": _traffic("corr_stream_headline", ["corr.hip", "ncc_internal.h"])}
+    else:
+        roof = {"kernel": "ncc_sat_build (sat_reduce + sat_carry + sat_downsweep)", "bound": "hbm",
+                "achieved": round(sat_rate, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(sat_rate / HBM_PEAK_GBS, 4),
+                "traffic": _traffic("sat_build_headline", ["sat.hip", "ncc_internal.h"])}
+
+    out = {
+        "metric": "NCC Gcoeff/s at 4096^2 u8, 16x16 template; SAT build GB/s at 4096^2",
+        "value": round(value, 2),
+        "unit": "Gcoeff/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": "headline: 4096x4096 u8 smooth noise (N(128,40^2), 9x9 box blur), one "
+                               "16x16 template cut from it; step = ncc_sat_build (S, Q int64) + "
+                               "ncc_correlate (4081x4081 float32 coefficients)",
+                   "image": [H, W], "template": [hT, wT], "n_templates": 1,
+                   "coefficients_per_step": coeffs},
+        "roofline": roof,
+        "components": comp,
+    }
+
+    # ------------------------------------------------ other workloads ----
+    if not args.no_extra:
+        ws = synth.make("sat")
+        simg = torch.from_numpy(ws["img"]).to(d)
+        rects = torch.from_numpy(ws["rects"]).to(d)
+        n = rects.shape[0]
+        bo1 = torch.empty((n,), dtype=torch.int64, device=d)
+        bo2 = torch.empty((n,), dtype=torch.int64, device=d)
+        psi, pr, pb1, pb2 = simg.data_ptr(), rects.data_ptr(), bo1.data_ptr(), bo2.data_ptr()
+
+        def sat2():
+            assert L.ncc_sat_build(psi, W, H, pS, pQ, sh) == 0
+
+        def boxes():
+            assert L.ncc_box(pS, W, H, pr, n, pb1, sh) == 0
+            assert L.ncc_box(pQ, W, H, pr, n, pb2, sh) == 0
+
+        _, (t_b, t_q) = time_calls([sat2, boxes], 20, 3, stream)
+        rate = sat_bytes / (t_b * 1e-3) / 1e9
+        out["sat_workload"] = {
+            "workload": "4096x4096 u8 uniform: ncc_sat_build, then 1,000,000 box queries on S and on Q",
+            "sat_build_ms": round(t_b, 5), "sat_build_GB/s": round(rate, 1),
+            "sat_build_frac_hbm": round(rate / HBM_PEAK_GBS, 4),
+            "box_2x1M_ms": round(t_q, 5), "box_Mquery/s": round(2 * n / (t_q * 1e-3) / 1e6, 1)}
+
+        wb = synth.make("bank")
+        bimg = torch.from_numpy(wb["img"]).to(d)
+        btpl = torch.from_numpy(wb["tpl"]).to(d)
+        nb = btpl.shape[0]
+        bcoef = torch.empty((nb, Ho, Wo), dtype=torch.float32, device=d)
+        pbi, pbt, pbc = bimg.data_ptr(), btpl.data_ptr(), bcoef.data_ptr()
+
+        def bank():
+            assert L.ncc_correlate(pbi, W, H, pbt, wT, hT, nb, None, pbc, sh) == 0
+
+        _, (t_k,) = time_calls([bank], 10, 2, stream)
+        bcoeffs = nb * coeffs
+        out_bytes = bcoeffs * 4 + H * W
+        bw = out_bytes / (t_k * 1e-3) / 1e9
+        mfma = bcoeffs * hT * wT * 2 / (t_k * 1e-3) / 1e12
+        out["bank_workload"] = {
+            "workload": "4096x4096 u8 smooth noise, 64 templates 16x16 (32 cut, 32 uniform): "
+                        "ncc_correlate on the int8 matrix cores",
+            "ms": round(t_k, 4), "Gcoeff/s": round(bcoeffs / (t_k * 1e-3) / 1e9, 1),
+            "hbm_GB/s": round(bw, 1), "frac_hbm": round(bw / HBM_PEAK_GBS, 4),
+            "int8_TOP/s": round(mfma, 1), "frac_mfma": round(mfma / INT8_MFMA_PEAK_TOPS, 4)}
+        for (x, y), t in zip(wb["cut_xy"], range(nb)):
+            assert abs(float(bcoef[t, y, x]) - 1.0) <= 1e-5
+        del bcoef
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(img_np, tpl_np[0])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
