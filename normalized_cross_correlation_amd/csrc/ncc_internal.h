@@ -10,9 +10,9 @@ namespace ncc {
 
 // ---------------------------------------------------------------- tables ---
 // Table build tiling: a workgroup of 4 wavefronts owns a tile of
-// SAT_SW columns x SAT_BH rows; each lane owns 4 adjacent columns and each
+// SAT_SW columns x SAT_BH rows; each lane owns 2 adjacent columns and each
 // wavefront 16 rows of the tile.
-constexpr int SAT_SW = 256;
+constexpr int SAT_SW = 128;
 constexpr int SAT_BH = 64;
 
 struct SatWork {

@@ -3,8 +3,8 @@
 // Area Tables" -- table definition, width analysis (uint32 row running sums,
 // int64 table) and the separable build (a row scan, then a column scan).
 //
-// MI355X design: reduce-then-scan over 256 x 64 tiles, with no waiting
-// between workgroups.
+// MI355X design: reduce-then-scan over 128-column x 64-row tiles, with no
+// waiting between workgroups.
 //   1. sat_reduce: each tile reads its bytes once and writes per-column sums
 //      of its band, per-row sums of its strip and its total (uint32/uint64,
 //      a few MB at 4096^2).
@@ -14,7 +14,8 @@
 //   3. sat_downsweep: each tile re-reads its bytes, forms the uint32 row
 //      running sums with a wavefront DPP scan plus the left carry, and adds
 //      them down each column into int64 running sums that start from the
-//      tile's top carry; S and Q are written once, as 16-byte stores.
+//      tile's top carry; S and Q are written once.  Lane l owns columns 2l
+//      and 2l+1, so one store instruction covers 1 KB of a table row.
 // The row partials never go to HBM: the only full-size traffic is one read
 // of the image per pass and one write of each table.
 #include "ncc_internal.h"
@@ -25,197 +26,262 @@ namespace {
 
 constexpr int WAVE_ROWS = SAT_BH / 4;  // rows per wavefront
 
-// Four pixels x..x+3 of row y as a little-endian dword; pixels outside the
+// Pixels x, x+1 of row y as the low 16 bits of a dword; pixels outside the
 // image read as 0.
 template <bool VEC>
-__device__ __forceinline__ uint32_t load4(const uint8_t *img, int W, int H,
-                                          int x, int y) {
+__device__ __forceinline__ uint32_t load2(const uint8_t *img, int W, int H, int x, int y) {
     if (y >= H) return 0u;
     const uint8_t *row = img + (size_t)y * W;
-    if (VEC) {
-        if (x + 3 < W) return *(const uint32_t *)(row + x);
-    }
+    if (VEC && x + 1 < W) return *(const uint16_t *)(row + x);
     uint32_t v = 0;
-#pragma unroll
-    for (int k = 0; k < 4; k++)
-        if (x + k < W) v |= (uint32_t)row[x + k] << (8 * k);
+    if (x < W) v = row[x];
+    if (x + 1 < W) v |= (uint32_t)row[x + 1] << 8;
     return v;
 }
 
-__device__ __forceinline__ void bytes_of(uint32_t p, uint32_t b[4], uint32_t q[4]) {
+// Bytes x .. x+15 of row y (zero outside the image).
+template <bool VEC>
+__device__ __forceinline__ uint4 load16(const uint8_t *img, int W, int H, int x, int y) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (y >= H || x >= W) return v;
+    const uint8_t *row = img + (size_t)y * W;
+    if (VEC && x + 15 < W) return *(const uint4 *)(row + x);
+    uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-        b[k] = (p >> (8 * k)) & 0xffu;
-        q[k] = b[k] * b[k];
-    }
+    for (int b = 0; b < 16; b++)
+        if (x + b < W) w[b >> 2] |= (uint32_t)row[x + b] << (8 * (b & 3));
+    return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ----------------------------------------------------------------- reduce --
+// Tile sums for the carries: per column of the band (colsum), per row of the
+// strip (rowtot) and the tile total.  A wavefront reduces one 128 x 64 tile:
+// lane l loads 16 columns (group l % 8) of the 8 rows 8*(l/8) .. +7.
 template <bool VEC>
-__global__ __launch_bounds__(256) void sat_reduce(const uint8_t *__restrict__ img,
-                                                  int W, int H, SatWork wk) {
-    const int s = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(256) void sat_reduce(const uint8_t *__restrict__ img, int W, int H,
+                                                  SatWork wk) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int x = s * SAT_SW + 4 * l;
-    const int y0 = b * SAT_BH + w * WAVE_ROWS;
+    const int s = blockIdx.x * 4 + w, b = blockIdx.y;
+    const int c8 = l & 7, rg = l >> 3;
+    const int x = s * SAT_SW + 16 * c8;
+    const int y = b * SAT_BH + 8 * rg;
+    const bool live = s < wk.nStrips;
+    uint4 px[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++)
+        px[r] = live ? load16<VEC>(img, W, H, x, y + r) : make_uint4(0, 0, 0, 0);
 
-    uint32_t c1[4] = {0, 0, 0, 0}, c2[4] = {0, 0, 0, 0};
-    uint32_t px[WAVE_ROWS];
+    // row sums: 16 columns per lane, then over the 8 lanes of a row group
+    // (DPP: swap pairs, swap pair-pairs, then lane 8g+7 adds lane 8g+3)
+    uint32_t cI[16], cQ[16];
 #pragma unroll
-    for (int r = 0; r < WAVE_ROWS; r++) px[r] = load4<VEC>(img, W, H, x, y0 + r);
+    for (int c = 0; c < 16; c++) cI[c] = cQ[c] = 0;
 #pragma unroll
-    for (int r = 0; r < WAVE_ROWS; r++) {
-        uint32_t bb[4], qq[4];
-        bytes_of(px[r], bb, qq);
-        uint32_t s1 = 0, s2 = 0;
+    for (int r = 0; r < 8; r++) {
+        const uint32_t d[4] = {px[r].x, px[r].y, px[r].z, px[r].w};
+        uint32_t a = 0, q = 0;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            c1[k] += bb[k];
-            c2[k] += qq[k];
-            s1 += bb[k];
-            s2 += qq[k];
+            a = dot4u(d[k], 0x01010101u, a);
+            q = dot4u(d[k], d[k], q);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t v = (d[k] >> (8 * e)) & 0xffu;
+                cI[4 * k + e] += v;
+                cQ[4 * k + e] += v * v;
+            }
         }
-        uint32_t t1 = wave_sum_u32(s1), t2 = wave_sum_u32(s2);
-        int y = y0 + r;
-        if (l == 0 && y < H) {
-            wk.rowtot[(size_t)y * wk.nStrips + s] = t1;
-            wk.rowtot[((size_t)H + y) * wk.nStrips + s] = t2;
+        a += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xf, 0xf, false);
+        q += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q, 0xB1, 0xf, 0xf, false);
+        a += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xf, 0xf, false);
+        q += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q, 0x4E, 0xf, 0xf, false);
+        a += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, DPP_ROW_SHR4, 0xf, 0xf, false);
+        q += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q, DPP_ROW_SHR4, 0xf, 0xf, false);
+        if (c8 == 7 && live && y + r < H) {
+            wk.rowtot[(size_t)(y + r) * wk.nStrips + s] = a;
+            wk.rowtot[((size_t)H + y + r) * wk.nStrips + s] = q;
         }
     }
 
-    __shared__ uint32_t part[2][4][SAT_SW];
+    // column sums: the 8 row groups of the wavefront meet in LDS
+    __shared__ uint32_t part[4][2][8][SAT_SW];
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-        part[0][w][4 * l + k] = c1[k];
-        part[1][w][4 * l + k] = c2[k];
+    for (int c = 0; c < 16; c += 4) {
+        *(uint4 *)&part[w][0][rg][16 * c8 + c] = make_uint4(cI[c], cI[c + 1], cI[c + 2], cI[c + 3]);
+        *(uint4 *)&part[w][1][rg][16 * c8 + c] = make_uint4(cQ[c], cQ[c + 1], cQ[c + 2], cQ[c + 3]);
     }
     __syncthreads();
-    // thread tid sums column tid of the tile over the four wavefronts
-    uint32_t v1 = part[0][0][tid] + part[0][1][tid] + part[0][2][tid] + part[0][3][tid];
-    uint32_t v2 = part[1][0][tid] + part[1][1][tid] + part[1][2][tid] + part[1][3][tid];
-    const int xc = s * SAT_SW + tid;
+    uint32_t sI[2] = {0, 0}, sQ[2] = {0, 0};
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        const uint2 u = *(const uint2 *)&part[w][0][r][2 * l];
+        const uint2 v = *(const uint2 *)&part[w][1][r][2 * l];
+        sI[0] += u.x;
+        sI[1] += u.y;
+        sQ[0] += v.x;
+        sQ[1] += v.y;
+    }
+    if (!live) return;  // wavefront-uniform; no barrier follows
+    const int xc = s * SAT_SW + 2 * l;
+    uint32_t *cs0 = wk.colsum + (size_t)b * W;
+    uint32_t *cs1 = wk.colsum + ((size_t)wk.nBands + b) * W;
     if (xc < W) {
-        wk.colsum[(size_t)b * W + xc] = v1;
-        wk.colsum[((size_t)wk.nBands + b) * W + xc] = v2;
+        cs0[xc] = sI[0];
+        cs1[xc] = sQ[0];
     }
-    // tile totals (uint64: 256 columns of up to 64*255^2)
-    uint64_t t1 = wave_incl_scan_u64((uint64_t)v1);
-    uint64_t t2 = wave_incl_scan_u64((uint64_t)v2);
-    __shared__ uint64_t wtot[2][4];
-    if (l == 63) {
-        wtot[0][w] = t1;
-        wtot[1][w] = t2;
+    if (xc + 1 < W) {
+        cs0[xc + 1] = sI[1];
+        cs1[xc + 1] = sQ[1];
     }
-    __syncthreads();
-    if (tid == 0) {
-        size_t o = (size_t)b * wk.nStrips + s;
-        wk.tiletot[o] = wtot[0][0] + wtot[0][1] + wtot[0][2] + wtot[0][3];
-        wk.tiletot[(size_t)wk.nBands * wk.nStrips + o] =
-            wtot[1][0] + wtot[1][1] + wtot[1][2] + wtot[1][3];
+    // tile totals: 128 columns of at most 64*255^2 fit uint32
+    const uint32_t tI = wave_sum_u32(sI[0] + sI[1]);
+    const uint32_t tQ = wave_sum_u32(sQ[0] + sQ[1]);
+    if (l == 0) {
+        const size_t o = (size_t)b * wk.nStrips + s;
+        wk.tiletot[o] = tI;
+        wk.tiletot[(size_t)wk.nBands * wk.nStrips + o] = tQ;
     }
 }
 
 // ------------------------------------------------------------------ carry --
-// Blocks [0, nColBlocks): one thread per column, exclusive scan down the
-// bands.  Blocks [nColBlocks, nColBlocks + nRowBlocks): one thread per row,
-// exclusive scan across the strips.  Last block: 2-D exclusive prefix of the
-// tile totals.
-__global__ __launch_bounds__(256) void sat_carry(int W, int H, SatWork wk,
-                                                 int nColBlocks, int nRowBlocks) {
+// Exclusive scans of the tile sums, in three roles by block index.
+//  cp:     a block scans 64 columns of one table down all bands: thread
+//          (column, quarter) loads its quarter of the bands at once, the four
+//          quarters are combined in LDS, then written back.
+//  lrow:   one thread per (table, row) scans the row's strip sums.
+//  corner: one block per table forms the 2-D exclusive prefix of the tile
+//          totals, in LDS when they fit.
+constexpr int CP_COLS = 64;
+constexpr int CP_MAXQ = 32;  // bands per quarter held in registers
+
+__global__ __launch_bounds__(256) void sat_carry(int W, int H, SatWork wk, int nCpBlocks,
+                                                 int nRowBlocks) {
     const int bid = blockIdx.x, tid = threadIdx.x;
-    if (bid < nColBlocks) {
-        const int x = bid * 256 + tid;
-        if (x >= W) return;
+    const int nB = wk.nBands, nS = wk.nStrips;
+    if (bid < nCpBlocks) {
+        const int colBlocks = (W + CP_COLS - 1) / CP_COLS;
+        const int t = bid / colBlocks;
+        const int x = (bid % colBlocks) * CP_COLS + (tid & (CP_COLS - 1));
+        const int qtr = tid / CP_COLS;  // 0..3
+        const uint32_t *__restrict__ cs = wk.colsum + (size_t)t * nB * W;
+        uint64_t *__restrict__ cp = wk.cp + (size_t)t * nB * W;
+        __shared__ uint64_t qsum[4][CP_COLS];
+        const int per = (nB + 3) / 4;
+        uint64_t run = 0;
+        // quarters longer than CP_MAXQ bands are walked in pieces
+        for (int p0 = 0; p0 < per; p0 += CP_MAXQ) {
+            uint32_t v[CP_MAXQ];
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-            const uint32_t *cs = wk.colsum + (size_t)t * wk.nBands * W;
-            uint64_t *cp = wk.cp + (size_t)t * wk.nBands * W;
-            uint64_t run = 0;
-            for (int b = 0; b < wk.nBands; b++) {
-                uint32_t v = cs[(size_t)b * W + x];
-                cp[(size_t)b * W + x] = run;
-                run += v;
+            for (int k = 0; k < CP_MAXQ; k++) {
+                const int bb = qtr * per + p0 + k;
+                v[k] = (p0 + k < per && bb < nB && x < W) ? cs[(size_t)bb * W + x] : 0u;
+            }
+#pragma unroll
+            for (int k = 0; k < CP_MAXQ; k++) run += v[k];
+        }
+        qsum[qtr][tid & (CP_COLS - 1)] = run;
+        __syncthreads();
+        uint64_t base = 0;
+        for (int q = 0; q < qtr; q++) base += qsum[q][tid & (CP_COLS - 1)];
+        if (x >= W) return;
+        for (int p0 = 0; p0 < per; p0 += CP_MAXQ) {
+            uint32_t v[CP_MAXQ];
+#pragma unroll
+            for (int k = 0; k < CP_MAXQ; k++) {
+                const int bb = qtr * per + p0 + k;
+                v[k] = (p0 + k < per && bb < nB) ? cs[(size_t)bb * W + x] : 0u;
+            }
+#pragma unroll
+            for (int k = 0; k < CP_MAXQ; k++) {
+                const int bb = qtr * per + p0 + k;
+                if (p0 + k < per && bb < nB) cp[(size_t)bb * W + x] = base;
+                base += v[k];
             }
         }
         return;
     }
-    if (bid < nColBlocks + nRowBlocks) {
-        const int y = (bid - nColBlocks) * 256 + tid;
-        if (y >= H) return;
+    if (bid < nCpBlocks + nRowBlocks) {
+        const int i = (bid - nCpBlocks) * 256 + tid;
+        if (i >= 2 * H) return;
+        const uint32_t *__restrict__ rt = wk.rowtot + (size_t)i * nS;
+        uint32_t *__restrict__ lr = wk.lrow + (size_t)i * nS;
+        uint32_t run = 0;
+        for (int s0 = 0; s0 < nS; s0 += 32) {
+            uint32_t v[32];
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-            const uint32_t *rt = wk.rowtot + ((size_t)t * H + y) * wk.nStrips;
-            uint32_t *lr = wk.lrow + ((size_t)t * H + y) * wk.nStrips;
-            uint32_t run = 0;
-            for (int s = 0; s < wk.nStrips; s++) {
-                uint32_t v = rt[s];
-                lr[s] = run;
-                run += v;
+            for (int k = 0; k < 32; k++) v[k] = (s0 + k < nS) ? rt[s0 + k] : 0u;
+#pragma unroll
+            for (int k = 0; k < 32; k++) {
+                if (s0 + k < nS) lr[s0 + k] = run;
+                run += v[k];
             }
         }
         return;
     }
     // corner[b][s] = sum over b' < b, s' < s of tiletot[b'][s']
-    for (int t = 0; t < 2; t++) {
-        const uint64_t *tt = wk.tiletot + (size_t)t * wk.nBands * wk.nStrips;
-        int64_t *cn = wk.corner + (size_t)t * wk.nBands * wk.nStrips;
-        for (int s = tid; s < wk.nStrips; s += 256) {
+    const int t = bid - nCpBlocks - nRowBlocks;
+    const uint64_t *tt = wk.tiletot + (size_t)t * nB * nS;
+    int64_t *cn = wk.corner + (size_t)t * nB * nS;
+    constexpr int LDS_MAX = 4096;
+    __shared__ uint64_t g[LDS_MAX];
+    if ((size_t)nB * nS <= LDS_MAX) {
+        for (int i = tid; i < nB * nS; i += 256) g[i] = tt[i];
+        __syncthreads();
+        for (int s = tid; s < nS; s += 256) {  // down the bands
             uint64_t run = 0;
-            for (int b = 0; b < wk.nBands; b++) {
-                uint64_t v = tt[(size_t)b * wk.nStrips + s];
-                cn[(size_t)b * wk.nStrips + s] = (int64_t)run;
+            for (int b = 0; b < nB; b++) {
+                const uint64_t v = g[b * nS + s];
+                g[b * nS + s] = run;
                 run += v;
             }
         }
         __syncthreads();
-        for (int b = tid; b < wk.nBands; b += 256) {
-            int64_t run = 0;
-            for (int s = 0; s < wk.nStrips; s++) {
-                int64_t v = cn[(size_t)b * wk.nStrips + s];
-                cn[(size_t)b * wk.nStrips + s] = run;
+        for (int b = tid; b < nB; b += 256) {  // across the strips
+            uint64_t run = 0;
+            for (int s = 0; s < nS; s++) {
+                const uint64_t v = g[b * nS + s];
+                g[b * nS + s] = run;
                 run += v;
             }
         }
         __syncthreads();
+        for (int i = tid; i < nB * nS; i += 256) cn[i] = (int64_t)g[i];
+        return;
+    }
+    for (int s = tid; s < nS; s += 256) {
+        uint64_t run = 0;
+        for (int b = 0; b < nB; b++) {
+            const uint64_t v = tt[(size_t)b * nS + s];
+            cn[(size_t)b * nS + s] = (int64_t)run;
+            run += v;
+        }
+    }
+    __syncthreads();
+    for (int b = tid; b < nB; b += 256) {
+        int64_t run = 0;
+        for (int s = 0; s < nS; s++) {
+            const int64_t v = cn[(size_t)b * nS + s];
+            cn[(size_t)b * nS + s] = run;
+            run += v;
+        }
     }
 }
 
 // ------------------------------------------------------------- downsweep --
-// Row partials R(x,y) = sum of row y over columns 0..x (uint32), for the
-// lane's four columns: left carry + wavefront exclusive scan + local scan.
-__device__ __forceinline__ void row_partials(uint32_t p, uint32_t left1, uint32_t left2,
-                                             uint32_t r1[4], uint32_t r2[4]) {
-    uint32_t bb[4], qq[4];
-    bytes_of(p, bb, qq);
-    r1[0] = bb[0];
-    r2[0] = qq[0];
-#pragma unroll
-    for (int k = 1; k < 4; k++) {
-        r1[k] = r1[k - 1] + bb[k];
-        r2[k] = r2[k - 1] + qq[k];
-    }
-    uint32_t e1 = wave_incl_scan_u32(r1[3]) - r1[3] + left1;
-    uint32_t e2 = wave_incl_scan_u32(r2[3]) - r2[3] + left2;
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        r1[k] += e1;
-        r2[k] += e2;
-    }
-}
-
+// Lane l of every wavefront owns columns x = 128*s + 2l and x + 1, so each
+// 16-byte store of a row lands next to its neighbours' (1 KB per wavefront).
 template <bool VEC>
-__global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__ img,
-                                                     int W, int H, SatWork wk,
-                                                     int64_t *__restrict__ S,
+__global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__ img, int W, int H,
+                                                     SatWork wk, int64_t *__restrict__ S,
                                                      int64_t *__restrict__ Q) {
     const int s = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int x = s * SAT_SW + 4 * l;
+    const int x = s * SAT_SW + 2 * l;
     const int y0 = b * SAT_BH + w * WAVE_ROWS;
 
     uint32_t px[WAVE_ROWS];
 #pragma unroll
-    for (int r = 0; r < WAVE_ROWS; r++) px[r] = load4<VEC>(img, W, H, x, y0 + r);
+    for (int r = 0; r < WAVE_ROWS; r++) px[r] = load2<VEC>(img, W, H, x, y0 + r);
     // left carries of the wavefront's rows: lane r holds row y0 + r
     uint32_t lc1 = 0, lc2 = 0;
     if (l < WAVE_ROWS && y0 + l < H) {
@@ -223,92 +289,85 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
         lc2 = wk.lrow[((size_t)H + y0 + l) * wk.nStrips + s];
     }
 
-    // pass 1: the wavefront's column totals of row partials
-    uint64_t ct1[4] = {0, 0, 0, 0}, ct2[4] = {0, 0, 0, 0};
+    // pass 1: uint32 row partials R(x,y) = sum over columns 0..x of row y
+    // (left carry + wavefront exclusive scan + own pixels), kept in registers,
+    // and their column totals over the wavefront's rows
+    uint32_t R1a[WAVE_ROWS], R1b[WAVE_ROWS], R2a[WAVE_ROWS], R2b[WAVE_ROWS];
+    uint64_t c1a = 0, c1b = 0, c2a = 0, c2b = 0;
 #pragma unroll
     for (int r = 0; r < WAVE_ROWS; r++) {
-        uint32_t r1[4], r2[4];
-        row_partials(px[r], (uint32_t)__builtin_amdgcn_readlane((int)lc1, r),
-                     (uint32_t)__builtin_amdgcn_readlane((int)lc2, r), r1, r2);
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            ct1[k] += r1[k];
-            ct2[k] += r2[k];
-        }
+        const uint32_t b0 = px[r] & 0xffu, b1 = (px[r] >> 8) & 0xffu;
+        const uint32_t p1 = b0 + b1, p2 = b0 * b0 + b1 * b1;
+        const uint32_t e1 = wave_incl_scan_u32(p1) - p1 +
+                            (uint32_t)__builtin_amdgcn_readlane((int)lc1, r);
+        const uint32_t e2 = wave_incl_scan_u32(p2) - p2 +
+                            (uint32_t)__builtin_amdgcn_readlane((int)lc2, r);
+        R1a[r] = e1 + b0;
+        R1b[r] = e1 + p1;
+        R2a[r] = e2 + b0 * b0;
+        R2b[r] = e2 + p2;
+        c1a += R1a[r];
+        c1b += R1b[r];
+        c2a += R2a[r];
+        c2b += R2b[r];
     }
-    __shared__ uint64_t part[2][4][SAT_SW];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        part[0][w][4 * l + k] = ct1[k];
-        part[1][w][4 * l + k] = ct2[k];
-    }
+    __shared__ uint64_t part[4][4][64];  // [wave][value][lane]
+    part[w][0][l] = c1a;
+    part[w][1][l] = c1b;
+    part[w][2][l] = c2a;
+    part[w][3][l] = c2b;
 
-    // top carry of the tile: corner + scan of the column sums above the band
-    uint64_t a1[4], a2[4];
+    // top carry: S(x, top - 1) = corner + scan of the column sums above the band
+    uint64_t s1a, s1b, s2a, s2b;
     {
         const uint64_t *cp1 = wk.cp + (size_t)b * W;
         const uint64_t *cp2 = wk.cp + ((size_t)wk.nBands + b) * W;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            a1[k] = (x + k < W) ? cp1[x + k] : 0;
-            a2[k] = (x + k < W) ? cp2[x + k] : 0;
-        }
-#pragma unroll
-        for (int k = 1; k < 4; k++) {
-            a1[k] += a1[k - 1];
-            a2[k] += a2[k - 1];
-        }
-        size_t co = (size_t)b * wk.nStrips + s;
-        uint64_t e1 = wave_incl_scan_u64(a1[3]) - a1[3] + (uint64_t)wk.corner[co];
-        uint64_t e2 = wave_incl_scan_u64(a2[3]) - a2[3] +
-                      (uint64_t)wk.corner[(size_t)wk.nBands * wk.nStrips + co];
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            a1[k] += e1;
-            a2[k] += e2;
-        }
+        const uint64_t u1a = x < W ? cp1[x] : 0, u1b = x + 1 < W ? cp1[x + 1] : 0;
+        const uint64_t u2a = x < W ? cp2[x] : 0, u2b = x + 1 < W ? cp2[x + 1] : 0;
+        const size_t co = (size_t)b * wk.nStrips + s;
+        const uint64_t p1 = u1a + u1b, p2 = u2a + u2b;
+        const uint64_t e1 = wave_incl_scan_u64(p1) - p1 + (uint64_t)wk.corner[co];
+        const uint64_t e2 = wave_incl_scan_u64(p2) - p2 +
+                            (uint64_t)wk.corner[(size_t)wk.nBands * wk.nStrips + co];
+        s1a = e1 + u1a;
+        s1b = e1 + p1;
+        s2a = e2 + u2a;
+        s2b = e2 + p2;
     }
     __syncthreads();
     for (int ww = 0; ww < w; ww++) {
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            a1[k] += part[0][ww][4 * l + k];
-            a2[k] += part[1][ww][4 * l + k];
-        }
+        s1a += part[ww][0][l];
+        s1b += part[ww][1][l];
+        s2a += part[ww][2][l];
+        s2b += part[ww][3][l];
     }
 
     // pass 2: running column sums, written row by row
+    typedef long long v2l __attribute__((ext_vector_type(2)));
+    const bool pair = VEC && x + 1 < W;
 #pragma unroll
     for (int r = 0; r < WAVE_ROWS; r++) {
         const int y = y0 + r;
         if (y >= H) break;
-        uint32_t r1[4], r2[4];
-        row_partials(px[r], (uint32_t)__builtin_amdgcn_readlane((int)lc1, r),
-                     (uint32_t)__builtin_amdgcn_readlane((int)lc2, r), r1, r2);
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            a1[k] += r1[k];
-            a2[k] += r2[k];
-        }
-        int64_t *srow = S + (size_t)y * W;
-        int64_t *qrow = Q + (size_t)y * W;
-        if (VEC && x + 3 < W) {
-            typedef long long v2l __attribute__((ext_vector_type(2)));
-            v2l s01 = {(long long)a1[0], (long long)a1[1]};
-            v2l s23 = {(long long)a1[2], (long long)a1[3]};
-            v2l q01 = {(long long)a2[0], (long long)a2[1]};
-            v2l q23 = {(long long)a2[2], (long long)a2[3]};
-            __builtin_nontemporal_store(s01, (v2l *)(srow + x));
-            __builtin_nontemporal_store(s23, (v2l *)(srow + x + 2));
-            __builtin_nontemporal_store(q01, (v2l *)(qrow + x));
-            __builtin_nontemporal_store(q23, (v2l *)(qrow + x + 2));
+        s1a += R1a[r];
+        s1b += R1b[r];
+        s2a += R2a[r];
+        s2b += R2b[r];
+        int64_t *srow = S + (size_t)y * W + x;
+        int64_t *qrow = Q + (size_t)y * W + x;
+        if (pair) {
+            const v2l sv = {(long long)s1a, (long long)s1b};
+            const v2l qv = {(long long)s2a, (long long)s2b};
+            __builtin_nontemporal_store(sv, (v2l *)srow);
+            __builtin_nontemporal_store(qv, (v2l *)qrow);
         } else {
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                if (x + k < W) {
-                    __builtin_nontemporal_store((long long)a1[k], (long long *)(srow + x + k));
-                    __builtin_nontemporal_store((long long)a2[k], (long long *)(qrow + x + k));
-                }
+            if (x < W) {
+                __builtin_nontemporal_store((long long)s1a, (long long *)srow);
+                __builtin_nontemporal_store((long long)s2a, (long long *)qrow);
+            }
+            if (x + 1 < W) {
+                __builtin_nontemporal_store((long long)s1b, (long long *)srow + 1);
+                __builtin_nontemporal_store((long long)s2b, (long long *)qrow + 1);
             }
         }
     }
@@ -347,21 +406,26 @@ SatWork sat_work_carve(void *base, int W, int H) {
 
 hipError_t sat_build_launch(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q,
                             const SatWork &wk, hipStream_t st) {
-    const bool vec = (W % 4 == 0) && (((uintptr_t)img & 3) == 0) &&
-                     (((uintptr_t)S & 15) == 0) && (((uintptr_t)Q & 15) == 0);
-    dim3 grid(wk.nStrips, wk.nBands), block(256);
-    if (vec)
-        hipLaunchKernelGGL(sat_reduce<true>, grid, block, 0, st, img, W, H, wk);
+    // 16-byte image rows for the reduce pass; even widths and 16-byte table
+    // rows for the paired loads and stores of the downsweep
+    const bool rvec = (W % 16 == 0) && (((uintptr_t)img & 15) == 0);
+    const bool dvec = (W % 2 == 0) && (((uintptr_t)img & 1) == 0) &&
+                      (((uintptr_t)S & 15) == 0) && (((uintptr_t)Q & 15) == 0);
+    dim3 block(256);
+    dim3 rgrid((wk.nStrips + 3) / 4, wk.nBands);
+    if (rvec)
+        hipLaunchKernelGGL(sat_reduce<true>, rgrid, block, 0, st, img, W, H, wk);
     else
-        hipLaunchKernelGGL(sat_reduce<false>, grid, block, 0, st, img, W, H, wk);
+        hipLaunchKernelGGL(sat_reduce<false>, rgrid, block, 0, st, img, W, H, wk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int nColBlocks = (W + 255) / 256, nRowBlocks = (H + 255) / 256;
-    hipLaunchKernelGGL(sat_carry, dim3(nColBlocks + nRowBlocks + 1), block, 0, st, W, H, wk,
-                       nColBlocks, nRowBlocks);
+    const int nCpBlocks = 2 * ((W + CP_COLS - 1) / CP_COLS), nRowBlocks = (2 * H + 255) / 256;
+    hipLaunchKernelGGL(sat_carry, dim3(nCpBlocks + nRowBlocks + 2), block, 0, st, W, H, wk,
+                       nCpBlocks, nRowBlocks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (vec)
+    dim3 grid(wk.nStrips, wk.nBands);
+    if (dvec)
         hipLaunchKernelGGL(sat_downsweep<true>, grid, block, 0, st, img, W, H, wk, S, Q);
     else
         hipLaunchKernelGGL(sat_downsweep<false>, grid, block, 0, st, img, W, H, wk, S, Q);
