@@ -59,68 +59,271 @@ __device__ __forceinline__ void store_sum(int32_t *p, int32_t v) {
 }
 
 // ------------------------------------------------------------- streaming --
-template <int WT4, int HT, int WAVES, int RS, int ALIGN>
+// Registers of one lane of the streaming kernel, which owns POS adjacent
+// output columns.
+template <int WT4, int HT, int POS>
+struct StreamState {
+    uint32_t tp[HT][WT4];      // template rows (zero-padded dwords)
+    uint32_t acc[POS][HT];     // SumIT rings: slot (row mod HT) of the output row
+    uint32_t pI[POS][HT];      // running column sums of HT rows ago
+    uint32_t pQ[POS][HT];
+    uint32_t PI[POS], PQ[POS]; // running column sums of window row sums
+    uint32_t sh[POS];          // byte offset of each window in the lane's first dword
+    uint32_t mlast, K, sumT;
+    float varTf;
+    float *out;                // the lane's first coefficient in the next finished row
+    int32_t *s0, *s1, *s2;     // its sums
+    bool wsum, wfirst;         // sums wanted; SumI / SumISq planes written by this call
+    bool pairs;                // wave-uniform: every lane's POS columns are distinct
+    int yrel;                  // output row (relative to the strip) finished next
+};
+
+// A wave-uniform value copied into a vector register: the template does not
+// fit the scalar register file, and uses of a spilled scalar cost a
+// v_readlane each.
+__device__ __forceinline__ uint32_t to_vgpr(uint32_t x) {
+    uint32_t r;
+    __asm__("v_mov_b32 %0, %1" : "=v"(r) : "s"(x));
+    return r;
+}
+
+typedef float f2u __attribute__((ext_vector_type(2), aligned(4)));
+typedef int i2u __attribute__((ext_vector_type(2), aligned(4)));
+
+template <int WT4, int HT, int POS>
+__device__ __forceinline__ float stream_coef(const StreamState<WT4, HT, POS> &st, uint32_t sumI,
+                                             uint32_t sumISq, uint32_t sumIT) {
+    if (HT * 4 * WT4 <= 256) {
+        // operands < 2^24 and |num| <= K^2 * 127.5^2 < 2^31: exact mod 2^32
+        const int32_t num = (int32_t)(__umul24(st.K, sumIT) - __umul24(sumI, st.sumT));
+        const uint32_t varI = __umul24(st.K, sumISq) - __umul24(sumI, sumI);
+        return ncc_coef((float)num, (float)varI, st.varTf);
+    } else {
+        const long long num = (long long)st.K * sumIT - (long long)sumI * st.sumT;
+        const long long varI = (long long)st.K * sumISq - (long long)sumI * sumI;
+        return ncc_coef((float)num, (float)varI, st.varTf);
+    }
+}
+
+// One image row: window row sums, products with all template rows, and the
+// output row whose window ends here.  PHASE 0: the strip's first HT image
+// rows, where template rows j > Q land above the strip and are skipped;
+// PHASE 2: the HT rows after the strip's last output row starts, where
+// template rows j <= Q land below the strip and are skipped (the windows of
+// the strip's last HT-1 output rows still end here); PHASE 1: all.
+template <int WT4, int HT, int POS, int Q, int PHASE>
+__device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
+                                           const uint32_t (&d)[WT4 + 1], int rowsOut, int Wo) {
+    uint32_t v[POS][WT4];
+#pragma unroll
+    for (int p = 0; p < POS; p++)
+#pragma unroll
+        for (int k = 0; k < WT4; k++) v[p][k] = align_bytes(d[k + 1], d[k], st.sh[p]);
+#pragma unroll
+    for (int p = 0; p < POS; p++) {
+        uint32_t hs = 0, hs2 = 0;
+#pragma unroll
+        for (int k = 0; k < WT4; k++) {
+            const uint32_t vm = (k == WT4 - 1) ? (v[p][k] & st.mlast) : v[p][k];
+            hs = dot4u(vm, 0x01010101u, hs);
+            hs2 = dot4u(vm, vm, hs2);
+        }
+        st.PI[p] += hs;
+        st.PQ[p] += hs2;
+    }
+    // k outer, j inner: consecutive dot4s feed different accumulators
+#pragma unroll
+    for (int k = 0; k < WT4; k++)
+#pragma unroll
+        for (int j = 0; j < HT; j++) {
+            if (PHASE == 0 && j > Q) continue;
+            if (PHASE == 2 && j <= Q) continue;
+            const int slot = (Q - j + HT) % HT;
+#pragma unroll
+            for (int p = 0; p < POS; p++)
+                st.acc[p][slot] = dot4u(v[p][k], st.tp[j][k], st.acc[p][slot]);
+        }
+    // Empty asm statements that read and "write" every accumulator close the
+    // row: without them the compiler defers each output's dot4s to where its
+    // sum is consumed, which serialises them into one chain per output and
+    // keeps 16 rows of image words live.
+#pragma unroll
+    for (int p = 0; p < POS; p++)
+#pragma unroll
+        for (int i = 0; i < HT; i++) __asm__ volatile("" : "+v"(st.acc[p][i]));
+    // nor may later rows' loads and byte shifts be hoisted into this one
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int fin = (Q + 1) % HT;
+    uint32_t sumIT[POS], sumI[POS], sumISq[POS];
+#pragma unroll
+    for (int p = 0; p < POS; p++) {
+        sumIT[p] = st.acc[p][fin];
+        st.acc[p][fin] = 0;
+        sumI[p] = st.PI[p] - st.pI[p][Q];
+        sumISq[p] = st.PQ[p] - st.pQ[p][Q];
+        st.pI[p][Q] = st.PI[p];
+        st.pQ[p][Q] = st.PQ[p];
+    }
+    if (PHASE == 0 && Q != HT - 1) return;  // no window ends here yet
+    // every lane holds real columns (lanes past the last one repeat it), so
+    // only the wave-uniform row test guards the stores
+    if (st.yrel < rowsOut) {
+        float g[POS];
+#pragma unroll
+        for (int p = 0; p < POS; p++) g[p] = stream_coef(st, sumI[p], sumISq[p], sumIT[p]);
+        if (POS == 2 && st.pairs) {
+            __builtin_nontemporal_store((f2u){g[0], g[POS - 1]}, (f2u *)st.out);
+            if (st.wsum) {
+                if (st.wfirst) {
+                    __builtin_nontemporal_store((i2u){(int)sumI[0], (int)sumI[POS - 1]}, (i2u *)st.s0);
+                    __builtin_nontemporal_store((i2u){(int)sumISq[0], (int)sumISq[POS - 1]},
+                                                (i2u *)st.s1);
+                }
+                __builtin_nontemporal_store((i2u){(int)sumIT[0], (int)sumIT[POS - 1]}, (i2u *)st.s2);
+            }
+        } else {
+            // edge lanes: column p of this lane is min(first + p, Wo - 1)
+#pragma unroll
+            for (int p = 0; p < POS; p++) {
+                const int dp = (int)(st.sh[p] - st.sh[0]);
+                store_coef(st.out + dp, g[p]);
+                if (st.wsum) {
+                    if (st.wfirst) {
+                        store_sum(st.s0 + dp, (int32_t)sumI[p]);
+                        store_sum(st.s1 + dp, (int32_t)sumISq[p]);
+                    }
+                    store_sum(st.s2 + dp, (int32_t)sumIT[p]);
+                }
+            }
+        }
+    }
+    st.yrel++;
+    st.out += Wo;
+    if (st.wsum) {
+        st.s0 += Wo;
+        st.s1 += Wo;
+        st.s2 += Wo;
+    }
+}
+
+// Rows Q .. HT-1 of a batch; the LDS reads of row Q+1 are issued before row
+// Q's arithmetic.
+template <int WT4, int HT, int POS, int Q, int PHASE>
+__device__ __forceinline__ void stream_rows(StreamState<WT4, HT, POS> &st, const uint32_t *rowbase,
+                                            int pitch, uint32_t (&d)[WT4 + 1], int rowsOut,
+                                            int Wo) {
+    uint32_t dn[WT4 + 1];
+    if constexpr (Q + 1 < HT) {
+#pragma unroll
+        for (int k = 0; k <= WT4; k++) dn[k] = rowbase[(Q + 1) * pitch + k];
+    }
+    stream_row<WT4, HT, POS, Q, PHASE>(st, d, rowsOut, Wo);
+    if constexpr (Q + 1 < HT) {
+#pragma unroll
+        for (int k = 0; k <= WT4; k++) d[k] = dn[k];
+        stream_rows<WT4, HT, POS, Q + 1, PHASE>(st, rowbase, pitch, d, rowsOut, Wo);
+    }
+}
+
+template <int WT4, int HT, int POS, int WAVES, int RS, int ALIGN, bool TALIGN>
 __global__ __launch_bounds__(WAVES * 64) void corr_stream(CorrArgs a, int t) {
-    constexpr int NT = WAVES * 64;                     // output columns per workgroup
-    constexpr int SEGB = NT + 4 * WT4 + 4;             // staged bytes per row
+    static_assert(RS % HT == 0, "strip height must be whole batches");
+    static_assert(POS == 1 || POS == 2, "one or two columns per lane");
+    constexpr int NT = WAVES * 64;                     // lanes per workgroup
+    constexpr int NC = NT * POS;                       // output columns per workgroup
+    constexpr int SEGB = NC + 4 * WT4 + 4;             // staged bytes per row
     constexpr int CH = (SEGB + 15) / 16;               // 16-byte chunks per row
     constexpr int PITCH = CH * 4 + 4;                  // dwords per LDS row
     constexpr int LOADS = (HT * CH + NT - 1) / NT;     // chunk loads per thread per batch
     __shared__ uint32_t buf[2][HT][PITCH];
 
     const int tid = threadIdx.x;
-    const int x0 = blockIdx.x * NT, y0 = blockIdx.y * RS;
-    const int x = x0 + tid;
-    const int db = tid >> 2;
-    const uint32_t sh = (uint32_t)(tid & 3);
+    const int x0 = blockIdx.x * NC, y0 = blockIdx.y * RS;
     const int rowsOut = min(RS, a.Ho - y0);
-    const int rowsIn = rowsOut + HT - 1;
-    const int nb = (rowsIn + HT - 1) / HT;
 
-    // template rows (wave-uniform), each zero-padded to WT4 dwords, and the
-    // template constants SumT, SumTSq, varT computed from them
+    StreamState<WT4, HT, POS> st;
+    // the lane's columns; lanes past the last output column compute (and
+    // store) that column again
+    const int xf = x0 + POS * tid;
+    const int xa = min(xf, a.Wo - 1);
+    const int lxa = xa - x0;   // byte offset of the first window in a staged row
+#pragma unroll
+    for (int p = 0; p < POS; p++) st.sh[p] = (uint32_t)(min(xf + p, a.Wo - 1) - x0 - (lxa & ~3));
+    st.pairs = x0 + NC <= a.Wo;
+
     const int wT = a.wT;
-    const uint32_t mlast = byte_mask(wT - 4 * (WT4 - 1));
+    st.mlast = byte_mask(wT - 4 * (WT4 - 1));
+    // template rows, zero-padded to WT4 dwords (wave-uniform)
     const uint8_t *T = a.tpl + (size_t)t * HT * wT;
-    uint32_t tp[HT][WT4];
-    if (wT == 4 * WT4 && (((uintptr_t)T & 3) == 0)) {
 #pragma unroll
-        for (int j = 0; j < HT; j++)
+    for (int j = 0; j < HT; j++)
 #pragma unroll
-            for (int k = 0; k < WT4; k++) tp[j][k] = ((const uint32_t *)(T + j * wT))[k];
-    } else {
-#pragma unroll
-        for (int j = 0; j < HT; j++)
-#pragma unroll
-            for (int k = 0; k < WT4; k++) {
+        for (int k = 0; k < WT4; k++) {
+            if (TALIGN) {
+                st.tp[j][k] = to_vgpr(((const uint32_t *)(T + j * 4 * WT4))[k]);
+            } else {
                 uint32_t v = 0;
 #pragma unroll
                 for (int b = 0; b < 4; b++)
                     if (4 * k + b < wT) v |= (uint32_t)T[j * wT + 4 * k + b] << (8 * b);
-                tp[j][k] = v;
+                st.tp[j][k] = v;
             }
-    }
+        }
     uint32_t sumT = 0, sumTSq = 0;
 #pragma unroll
     for (int j = 0; j < HT; j++)
 #pragma unroll
         for (int k = 0; k < WT4; k++) {
-            sumT = dot4u(tp[j][k], 0x01010101u, sumT);
-            sumTSq = dot4u(tp[j][k], tp[j][k], sumTSq);
+            sumT = dot4u(st.tp[j][k], 0x01010101u, sumT);
+            sumTSq = dot4u(st.tp[j][k], st.tp[j][k], sumTSq);
         }
-    const uint32_t K = (uint32_t)(wT * HT);
+    st.K = (uint32_t)(wT * HT);
+    st.sumT = sumT;
     // varT <= K^2 * 127.5^2 < 2^32 for K <= 514
-    const float varTf = (float)(K * sumTSq - sumT * sumT);
-
-    // staging: chunk i of the batch -> row i / CH, bytes 16 * (i % CH)
-    uint4 pre[LOADS];
-    auto fetch = [&](int bt) {
+    st.varTf = (float)(st.K * sumTSq - sumT * sumT);
 #pragma unroll
-        for (int u = 0; u < LOADS; u++) {
-            const int i = tid + u * NT;
-            const int r = i / CH, c = i % CH;
-            pre[u] = (i < HT * CH) ? load16<ALIGN>(a.img, a.W, a.H, x0 + 16 * c, y0 + bt * HT + r)
-                                   : make_uint4(0, 0, 0, 0);
+    for (int p = 0; p < POS; p++) {
+        st.PI[p] = st.PQ[p] = 0;
+#pragma unroll
+        for (int i = 0; i < HT; i++) st.acc[p][i] = st.pI[p][i] = st.pQ[p][i] = 0;
+    }
+    st.yrel = 0;
+    const size_t plane = (size_t)a.Ho * a.Wo;
+    const size_t o0 = (size_t)y0 * a.Wo + xa;
+    st.out = a.coef + (size_t)t * plane + o0;
+    st.wsum = a.sums != nullptr;
+    st.wfirst = t == 0;
+    // only dereferenced when st.wsum (and st.wfirst for s0, s1)
+    int32_t *sb = st.wsum ? a.sums : (int32_t *)a.coef;
+    st.s0 = sb + o0;
+    st.s1 = sb + plane + o0;
+    st.s2 = sb + (size_t)(2 + t) * plane + o0;
+
+    // staging: chunk i of the batch -> row i / CH, bytes 16 * (i % CH); a
+    // batch whose staged rectangle lies inside the image loads without any
+    // per-byte test (wave-uniform choice)
+    uint4 pre[LOADS];
+    const bool colsIn = ALIGN == 16 && x0 + 16 * CH <= a.W;
+    auto fetch = [&](int bt) {
+        const bool inside = colsIn && y0 + (bt + 1) * HT <= a.H;
+        if (inside) {
+#pragma unroll
+            for (int u = 0; u < LOADS; u++) {
+                const int i = tid + u * NT;
+                const int r = i / CH, c = i % CH;
+                pre[u] = (i < HT * CH)
+                             ? *(const uint4 *)(a.img + (size_t)(y0 + bt * HT + r) * a.W + x0 + 16 * c)
+                             : make_uint4(0, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < LOADS; u++) {
+                const int i = tid + u * NT;
+                const int r = i / CH, c = i % CH;
+                pre[u] = (i < HT * CH)
+                             ? load16<ALIGN>(a.img, a.W, a.H, x0 + 16 * c, y0 + bt * HT + r)
+                             : make_uint4(0, 0, 0, 0);
+            }
         }
     };
     auto put = [&](int bt) {
@@ -134,80 +337,41 @@ __global__ __launch_bounds__(WAVES * 64) void corr_stream(CorrArgs a, int t) {
         }
     };
 
-    uint32_t acc[HT], pI[HT], pQ[HT];
-#pragma unroll
-    for (int i = 0; i < HT; i++) acc[i] = pI[i] = pQ[i] = 0;
-    uint32_t PI = 0, PQ = 0;
-
+    // batches of HT image rows: the first (PHASE 0), RS/HT - 1 full ones, and
+    // one past the last output row's start (PHASE 2); a strip cut short by the
+    // image bottom runs its last batches in PHASE 1 and discards what lands
+    // past rowsOut
+    const bool full = rowsOut == RS;
+    const int nb = full ? RS / HT + 1 : (rowsOut + 2 * HT - 2) / HT;
+    const int nmid = full ? nb - 1 : nb;  // batches before the PHASE 2 one
+    const uint32_t *rowbase0 = &buf[0][0][lxa >> 2];
+    uint32_t d[WT4 + 1];
     fetch(0);
     put(0);
     __syncthreads();
-    for (int bt = 0; bt < nb; bt++) {
+    // batch 0
+    if (nb > 1) fetch(1);
+#pragma unroll
+    for (int k = 0; k <= WT4; k++) d[k] = rowbase0[k];
+    stream_rows<WT4, HT, POS, 0, 0>(st, rowbase0, PITCH, d, rowsOut, a.Wo);
+    if (nb > 1) put(1);
+    __syncthreads();
+    // full batches
+    for (int bt = 1; bt < nmid; bt++) {
         if (bt + 1 < nb) fetch(bt + 1);
+        const uint32_t *rowbase = rowbase0 + (bt & 1) * HT * PITCH;
 #pragma unroll
-        for (int q = 0; q < HT; q++) {
-            const uint32_t *rowp = &buf[bt & 1][q][db];
-            uint32_t d[WT4 + 1];
-#pragma unroll
-            for (int k = 0; k <= WT4; k++) d[k] = rowp[k];
-            uint32_t v[WT4];
-#pragma unroll
-            for (int k = 0; k < WT4; k++) v[k] = align_bytes(d[k + 1], d[k], sh);
-            // window row sums of I and I^2
-            uint32_t hs = 0, hs2 = 0;
-#pragma unroll
-            for (int k = 0; k < WT4; k++) {
-                const uint32_t m = (k == WT4 - 1) ? mlast : 0xffffffffu;
-                hs = dot4u(v[k], 0x01010101u & m, hs);
-                hs2 = dot4u(v[k], v[k] & m, hs2);
-            }
-            PI += hs;
-            PQ += hs2;
-            // products with every template row
-#pragma unroll
-            for (int j = 0; j < HT; j++) {
-                const int slot = (q - j + HT) % HT;
-                uint32_t s = acc[slot];
-#pragma unroll
-                for (int k = 0; k < WT4; k++) s = dot4u(v[k], tp[j][k], s);
-                acc[slot] = s;
-            }
-            // output row whose window ends at this image row
-            const int fin = (q + 1) % HT;
-            const uint32_t sumIT = acc[fin];
-            acc[fin] = 0;
-            const uint32_t sumI = PI - pI[q];
-            const uint32_t sumISq = PQ - pQ[q];
-            pI[q] = PI;
-            pQ[q] = PQ;
-            const int rho = bt * HT + q;  // image row relative to y0
-            const int yo = y0 + rho - (HT - 1);
-            if (rho >= HT - 1 && rho - (HT - 1) < rowsOut && x < a.Wo) {
-                float g;
-                if (HT * 4 * WT4 <= 363) {
-                    // |num| <= K^2 * 127.5^2 < 2^31 and varI < 2^32: exact mod 2^32
-                    const int32_t num = (int32_t)(K * sumIT - sumI * sumT);
-                    const uint32_t varI = K * sumISq - sumI * sumI;
-                    g = ncc_coef((float)num, (float)varI, varTf);
-                } else {
-                    const long long num = (long long)K * sumIT - (long long)sumI * (long long)sumT;
-                    const long long varI = (long long)K * sumISq - (long long)sumI * (long long)sumI;
-                    g = ncc_coef((float)num, (float)varI, varTf);
-                }
-                const size_t plane = (size_t)a.Ho * a.Wo;
-                const size_t o = (size_t)yo * a.Wo + x;
-                store_coef(a.coef + (size_t)t * plane + o, g);
-                if (a.sums) {
-                    if (t == 0) {
-                        store_sum(a.sums + o, (int32_t)sumI);
-                        store_sum(a.sums + plane + o, (int32_t)sumISq);
-                    }
-                    store_sum(a.sums + (size_t)(2 + t) * plane + o, (int32_t)sumIT);
-                }
-            }
-        }
+        for (int k = 0; k <= WT4; k++) d[k] = rowbase[k];
+        stream_rows<WT4, HT, POS, 0, 1>(st, rowbase, PITCH, d, rowsOut, a.Wo);
         if (bt + 1 < nb) put(bt + 1);
         __syncthreads();
+    }
+    // the batch past a full strip's last output row start
+    if (full) {
+        const uint32_t *rowbase = rowbase0 + ((nb - 1) & 1) * HT * PITCH;
+#pragma unroll
+        for (int k = 0; k <= WT4; k++) d[k] = rowbase[k];
+        stream_rows<WT4, HT, POS, 0, 2>(st, rowbase, PITCH, d, rowsOut, a.Wo);
     }
 }
 
@@ -313,23 +477,41 @@ __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int
     }
 }
 
-constexpr int STREAM_WAVES = 4;
-constexpr int STREAM_RS = 128;
+#ifndef NCC_STREAM_WAVES
+#define NCC_STREAM_WAVES 4
+#endif
+#ifndef NCC_STREAM_RS
+#define NCC_STREAM_RS 64
+#endif
+#ifndef NCC_STREAM_POS
+#define NCC_STREAM_POS 2
+#endif
+constexpr int STREAM_WAVES = NCC_STREAM_WAVES;  // wavefronts per workgroup
+constexpr int STREAM_RS = NCC_STREAM_RS;        // output rows per strip
+constexpr int STREAM_POS = NCC_STREAM_POS;      // output columns per lane
+
+template <int WT4, int HT, bool TALIGN>
+hipError_t launch_stream_t(const CorrArgs &a, int t, hipStream_t st) {
+    constexpr int NC = STREAM_WAVES * 64 * STREAM_POS;
+    dim3 grid((a.Wo + NC - 1) / NC, (a.Ho + STREAM_RS - 1) / STREAM_RS), block(STREAM_WAVES * 64);
+    if (a.W % 16 == 0 && ((uintptr_t)a.img & 15) == 0)
+        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, STREAM_RS, 16, TALIGN>),
+                           grid, block, 0, st, a, t);
+    else if (a.W % 4 == 0 && ((uintptr_t)a.img & 3) == 0)
+        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, STREAM_RS, 4, TALIGN>),
+                           grid, block, 0, st, a, t);
+    else
+        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, STREAM_RS, 1, TALIGN>),
+                           grid, block, 0, st, a, t);
+    return hipGetLastError();
+}
 
 template <int WT4, int HT>
 hipError_t launch_stream(const CorrArgs &a, int t, hipStream_t st) {
-    constexpr int NT = STREAM_WAVES * 64;
-    dim3 grid((a.Wo + NT - 1) / NT, (a.Ho + STREAM_RS - 1) / STREAM_RS);
-    if (a.W % 16 == 0 && ((uintptr_t)a.img & 15) == 0)
-        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_WAVES, STREAM_RS, 16>), grid, dim3(NT), 0,
-                           st, a, t);
-    else if (a.W % 4 == 0 && ((uintptr_t)a.img & 3) == 0)
-        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_WAVES, STREAM_RS, 4>), grid, dim3(NT), 0,
-                           st, a, t);
-    else
-        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_WAVES, STREAM_RS, 1>), grid, dim3(NT), 0,
-                           st, a, t);
-    return hipGetLastError();
+    // whole-dword template rows at a 4-byte aligned address load as dwords
+    if (a.wT == 4 * WT4 && ((uintptr_t)a.tpl & 3) == 0)
+        return launch_stream_t<WT4, HT, true>(a, t, st);
+    return launch_stream_t<WT4, HT, false>(a, t, st);
 }
 
 void generic_geometry(int wT, int hT, int *pitch, int *rowsT) {
