@@ -9,8 +9,9 @@
 //   SumIT = SIT' + 128*SumI + 128*SumT - 16384*K.
 // The coefficient's numerator is then
 //   num = K*SIT' + SumI*(128K - SumT) + (128K*SumT - 16384K^2),
-// evaluated modulo 2^32: exact, since |num| <= K^2 * 127.5^2 < 2^31 for the
-// K <= 256 this kernel takes.
+// evaluated with 24-bit multiplies modulo 2^32: exact, since every factor
+// fits 24 signed bits and |num| <= K^2 * 127.5^2 < 2^31 for the K <= 256
+// this kernel takes.
 //
 // Operand layout (16x16x64, checked on the device): lane 16*g + m of the A
 // operand holds 16 bytes of row m, lane 16*g + n of B the same 16 k-slots of
@@ -18,12 +19,17 @@
 // The k order inside the 64 is the same for A and B, so chunk c = 4*kstep + g
 // is a 16-byte piece of one template row (row c / NB16, bytes 16*(c % NB16)).
 //
-// A workgroup (4 wavefronts) owns 64 x 16 output positions and up to 64
-// templates (4 blocks of 16).  The image tile + halo is staged in LDS; each
-// wavefront takes groups of 16 positions of one row (the A rows), byte-aligns
-// and offsets their chunks, and runs KSTEPS x 4 MFMAs.  Window sums SumI and
-// SumISq of the 16 positions come from the same operands (v_dot4_i32_i8),
-// once for all templates.
+// A workgroup (4 wavefronts) owns 64 x 16 output positions and NB blocks of
+// 16 templates.  It stages the image tile + halo in LDS as int8, then
+//   1. window statistics: SumI and 1/sqrt(varI) of its 1024 positions (row
+//      window sums per image row, then the hT-row sums), kept in LDS;
+//   2. per row of 64 positions (4 groups of 16 A rows): byte-aligns the
+//      chunks, runs KSTEPS x 4 MFMAs per block of 16 templates, turns each
+//      result into a coefficient with the statistics of its position and
+//      template, and writes them through a per-wavefront LDS transpose so
+//      that each store instruction covers 256 contiguous bytes of each of 4
+//      template maps (the MFMA result layout spreads one instruction over 16
+//      maps, 64 bytes each, which the memory system serves poorly).
 #include "ncc_internal.h"
 
 namespace ncc {
@@ -32,20 +38,42 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef int i4u __attribute__((ext_vector_type(4), aligned(4)));
 
 constexpr int BX = 64;  // positions per workgroup row
 constexpr int BY = 16;  // rows per workgroup
+constexpr int MAXR = BY + 15;  // tile rows for hT <= 16
+constexpr int OBP = BX + 4;    // row pitch (floats) of the output transpose buffer
 
-template <int KSTEPS, bool FULL>
-__global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch, int rowsT) {
-    extern __shared__ uint32_t tile[];  // rowsT x pitch bytes
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+template <int KSTEPS, int NB, bool FULLT>
+__global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch, int rowsT,
+                                                 int g0, int ntx, int nty, int nz) {
+    extern __shared__ uint32_t tile[];  // rowsT x pitch bytes of I' = I ^ 0x80
+    __shared__ int hsI[MAXR][BX];       // row window sums of I'
+    __shared__ int hsQ[MAXR][BX];       // row window sums of I'^2
+    __shared__ int sIs[BY][BX];         // SumI per position
+    __shared__ float rIs[BY][BX];       // 1/sqrt(varI) per position, 0 if varI == 0
+    __shared__ float obuf[4][16][OBP];  // per wavefront: 16 templates x 64 positions
+    // Workgroups go to the 8 XCDs round-robin in launch order; tile k/8 of
+    // XCD k%8's contiguous range keeps each XCD's L2 writing one compact
+    // stretch of the output maps (several times the write bandwidth of
+    // interleaved tiles).
+    const int ntiles = ntx * nty * nz, per = (ntiles + 7) / 8;
+    const int tix = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (tix >= ntiles) return;
+    const int bz = tix / (ntx * nty), bxy = tix % (ntx * nty);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int g = l >> 4, m = l & 15;
-    const int x0 = blockIdx.x * BX, y0 = blockIdx.y * BY;
+    const int x0 = (bxy % ntx) * BX, y0 = (bxy / ntx) * BY;
     const int pw = pitch / 4;
     const int K = a.wT * a.hT;
+    const int wt4 = (a.wT + 3) / 4;
 
-    // stage tile + halo (bytes outside the image are 0)
+    // ---- stage the tile + halo as int8 (bytes outside the image are 0 ^ 0x80)
     for (int i = tid; i < rowsT * pw; i += 256) {
         const int r = i / pw, c = i % pw;
         const int y = y0 + r, xb = x0 + 4 * c;
@@ -60,28 +88,21 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
                     if (xb + b < a.W) v |= (uint32_t)row[xb + b] << (8 * b);
             }
         }
-        tile[i] = v;
+        tile[i] = v ^ 0x80808080u;
     }
 
-    // B operands and per-template constants of this workgroup's 4 blocks
-    const int gbase = blockIdx.z * 4;
-    const int ngroups = (a.nTpl + 15) / 16;
-    v4i bop[4][KSTEPS];
-    int ca[4], cb[4];
-    float rT[4];
+    // ---- B operands and per-template constants of the NB blocks
+    v4i bop[NB][KSTEPS];
+    int ca[NB], cb[NB];
+    float rT[NB];
 #pragma unroll
-    for (int nb = 0; nb < 4; nb++) {
-        const int gg = gbase + nb;
-        const int tt = gg * 16 + m;  // this lane's template in block nb (lane n = m)
-        if (gg < ngroups) {
+    for (int nb = 0; nb < NB; nb++) {
+        const int gg = g0 + bz * NB + nb;
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ks++)
-                bop[nb][ks] = *(const v4i *)(a.mfma + (((size_t)gg * KSTEPS + ks) * 64 + l) * 16);
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ks++) bop[nb][ks] = (v4i){0, 0, 0, 0};
-        }
-        if (gg < ngroups && tt < a.nTpl) {
+        for (int ks = 0; ks < KSTEPS; ks++)
+            bop[nb][ks] = *(const v4i *)(a.mfma + (((size_t)gg * KSTEPS + ks) * 64 + l) * 16);
+        const int tt = gg * 16 + m;  // this lane's template in block nb
+        if (FULLT || tt < a.nTpl) {
             const TStat ts = a.stats[tt];
             const int sT = (int)ts.sumT;
             ca[nb] = 128 * K - sT;
@@ -92,124 +113,158 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
             rT[nb] = 0.0f;
         }
     }
-    const int nblk = min(4, ngroups - gbase);
+    __syncthreads();
 
-    // byte masks of this lane's chunks (only for shapes that pad)
-    uint32_t msk[KSTEPS][4];
+    // ---- 1. window statistics of the tile's positions
+    // row window sums: (image row r, column c) pairs, 4 per thread pass
+    const int rowsHs = BY + a.hT - 1;
+    const uint32_t mlast = byte_mask(a.wT - 4 * (wt4 - 1));
+    for (int i = tid; i < rowsHs * BX; i += 256) {
+        const int r = i / BX, c = i % BX;
+        const uint32_t *p = tile + r * pw + (c >> 2);
+        const uint32_t sh = (uint32_t)(c & 3);
+        int s1 = 0, s2 = 0;
+        uint32_t lo = p[0];
+        for (int k = 0; k < wt4; k++) {
+            const uint32_t hi = p[k + 1];
+            uint32_t v = align_bytes(hi, lo, sh);
+            // padding bytes must count as I' = 0, not as pixels
+            if (k == wt4 - 1) v &= mlast;
+            s1 = sdot4(v, 0x01010101u, s1);
+            s2 = sdot4(v, v, s2);
+            lo = hi;
+        }
+        hsI[r][c] = s1;
+        hsQ[r][c] = s2;
+    }
+    __syncthreads();
+    {
+        // thread (c, rq): output rows 4rq .. 4rq+3 of column c
+        const int c = tid & 63, rq = tid >> 6;
+        int s1 = 0, s2 = 0;
+        for (int j = 0; j < a.hT; j++) {
+            s1 += hsI[4 * rq + j][c];
+            s2 += hsQ[4 * rq + j][c];
+        }
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ks++) {
-        const int c = 4 * ks + g, j = c / nb16, ib = c % nb16;
-        const int nbytes = (j < a.hT) ? min(16, a.wT - 16 * ib) : 0;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const int nbk = nbytes - 4 * k;
-            msk[ks][k] = nbk <= 0 ? 0u : byte_mask(nbk);
+        for (int o = 0; o < 4; o++) {
+            if (o > 0) {
+                s1 += hsI[4 * rq + o + a.hT - 1][c] - hsI[4 * rq + o - 1][c];
+                s2 += hsQ[4 * rq + o + a.hT - 1][c] - hsQ[4 * rq + o - 1][c];
+            }
+            // SumI = sum I' + 128K;  SumISq = sum I'^2 + 256 sum I' + 16384K
+            const int sumI = s1 + 128 * K;
+            const int sumISq = s2 + 256 * s1 + 16384 * K;
+            const unsigned varI = (unsigned)K * (unsigned)sumISq - (unsigned)sumI * (unsigned)sumI;
+            sIs[4 * rq + o][c] = sumI;
+            rIs[4 * rq + o][c] = varI ? __builtin_amdgcn_rsqf((float)varI) : 0.0f;
+            if (a.sums && bz == 0 && g0 == 0) {
+                const int y = y0 + 4 * rq + o, x = x0 + c;
+                if (y < a.Ho && x < a.Wo) {
+                    const size_t plane = (size_t)a.Ho * a.Wo, oo = (size_t)y * a.Wo + x;
+                    __builtin_nontemporal_store(sumI, a.sums + oo);
+                    __builtin_nontemporal_store(sumISq, a.sums + plane + oo);
+                }
+            }
         }
     }
     __syncthreads();
 
+    // ---- 2. the contraction: each wavefront takes whole rows of 64 positions
+    // (4 groups of 16, the A rows) and, per block of 16 templates, turns the
+    // MFMA results into coefficients, transposes them through its LDS buffer
+    // and writes 256 contiguous bytes per template row.
+    float *ob = &obuf[w][0][0];
     const size_t plane = (size_t)a.Ho * a.Wo;
-    // 16 rows x 4 groups of 16 positions; wavefront w takes rows w, w+4, ...
-    for (int it = 0; it < BY / 4 * (BX / 16); it++) {
-        const int yy = w + 4 * (it / (BX / 16));
-        const int xg = 16 * (it % (BX / 16));
+    const bool whole = x0 + BX <= a.Wo;  // every column of the tile is an output
+    for (int yy = w; yy < BY; yy += 4) {
         const int y = y0 + yy;
         if (y >= a.Ho) break;
-        if (x0 + xg >= a.Wo) continue;
-
-        // A operands: row m = position xg + m, chunk c = 4*ks + g
-        v4i A[KSTEPS];
-        int sI = 0, sQ = 0;
-        const int px = xg + m;
+        // A operands: group mg, row m = position 16*mg + m, chunk c = 4*ks + g
+        v4i A[4][KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ks++) {
-            const int c = 4 * ks + g, j = c / nb16, ib = c % nb16;
-            const int jj = j < a.hT ? j : 0;
-            const int off = (yy + jj) * pitch + px + 16 * ib;
-            const uint32_t *p = tile + (off >> 2);
-            const uint32_t sh = (uint32_t)(off & 3);
-            uint32_t d0 = p[0], d1 = p[1], d2 = p[2], d3 = p[3], d4 = p[4];
-            uint32_t v[4];
-            v[0] = align_bytes(d1, d0, sh) ^ 0x80808080u;
-            v[1] = align_bytes(d2, d1, sh) ^ 0x80808080u;
-            v[2] = align_bytes(d3, d2, sh) ^ 0x80808080u;
-            v[3] = align_bytes(d4, d3, sh) ^ 0x80808080u;
+        for (int mg = 0; mg < 4; mg++)
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint32_t vm = FULL ? v[k] : (v[k] & msk[ks][k]);
-                sI = __builtin_amdgcn_sdot4((int)vm, 0x01010101, sI, false);
-                sQ = __builtin_amdgcn_sdot4((int)vm, (int)vm, sQ, false);
+            for (int ks = 0; ks < KSTEPS; ks++) {
+                const int c = 4 * ks + g, j = c / nb16, ib = c % nb16;
+                const int jj = j < a.hT ? j : 0;  // padding chunks meet zero template bytes
+                const int off = (yy + jj) * pitch + 16 * mg + m + 16 * ib;
+                const uint32_t *p = tile + (off >> 2);
+                const uint32_t sh = (uint32_t)(off & 3);
+                const uint32_t d0 = p[0], d1 = p[1], d2 = p[2], d3 = p[3], d4 = p[4];
+                A[mg][ks] = (v4i){(int)align_bytes(d1, d0, sh), (int)align_bytes(d2, d1, sh),
+                                  (int)align_bytes(d3, d2, sh), (int)align_bytes(d4, d3, sh)};
             }
-            A[ks] = (v4i){(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+        // statistics of this lane's result rows: positions 16*mg + 4g .. +3
+        int4 sI4[4];
+        float4 rI4[4];
+#pragma unroll
+        for (int mg = 0; mg < 4; mg++) {
+            sI4[mg] = *(const int4 *)&sIs[yy][16 * mg + 4 * g];
+            rI4[mg] = *(const float4 *)&rIs[yy][16 * mg + 4 * g];
         }
-        // sums over the four chunk groups of position m
-        sI += __shfl_xor(sI, 16);
-        sI += __shfl_xor(sI, 32);
-        sQ += __shfl_xor(sQ, 16);
-        sQ += __shfl_xor(sQ, 32);
-        const int sumI = sI + 128 * K;
-        const int sumISq = sQ + 256 * sI + 16384 * K;
-        const unsigned varI = (unsigned)K * (unsigned)sumISq - (unsigned)sumI * (unsigned)sumI;
-        const float rI = varI ? __builtin_amdgcn_rsqf((float)varI) : 0.0f;
-        // this lane's result rows are positions 4g .. 4g+3
-        int sumIi[4];
-        float rIi[4];
+        const size_t orow = (size_t)y * a.Wo + x0;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            sumIi[i] = __shfl(sumI, 4 * g + i);
-            rIi[i] = __shfl(rI, 4 * g + i);
-        }
-        const int xb = x0 + xg + 4 * g;  // first output column of this lane
-        const size_t orow = (size_t)y * a.Wo;
-        if (a.sums && blockIdx.z == 0 && g == 0) {
-            const int xm = x0 + xg + m;
-            if (xm < a.Wo) {
-                __builtin_nontemporal_store(sumI, a.sums + orow + xm);
-                __builtin_nontemporal_store(sumISq, a.sums + plane + orow + xm);
+        for (int nb = 0; nb < NB; nb++) {
+            v4i acc[4];
+#pragma unroll
+            for (int mg = 0; mg < 4; mg++) acc[mg] = (v4i){0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ks++)
+#pragma unroll
+                for (int mg = 0; mg < 4; mg++)
+                    acc[mg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[mg][ks], bop[nb][ks], acc[mg],
+                                                                    0, 0, 0);
+            // coefficients into ob[template m][position]
+#pragma unroll
+            for (int mg = 0; mg < 4; mg++) {
+                const int sIi[4] = {sI4[mg].x, sI4[mg].y, sI4[mg].z, sI4[mg].w};
+                const float rIi[4] = {rI4[mg].x, rI4[mg].y, rI4[mg].z, rI4[mg].w};
+                float gv[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int num = __mul24(K, acc[mg][i]) + __mul24(sIi[i], ca[nb]) + cb[nb];
+                    gv[i] = __builtin_amdgcn_fmed3f((float)num * (rIi[i] * rT[nb]), -1.0f, 1.0f);
+                }
+                *(float4 *)&ob[m * OBP + 16 * mg + 4 * g] = make_float4(gv[0], gv[1], gv[2], gv[3]);
+                if (a.sums) {
+                    const int tt = (g0 + bz * NB + nb) * 16 + m;
+                    const int xb = x0 + 16 * mg + 4 * g;
+                    if (FULLT || tt < a.nTpl) {
+                        const int sT = 128 * K - ca[nb];
+                        int32_t *sd = a.sums + (size_t)(2 + tt) * plane + (size_t)y * a.Wo + xb;
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            if (xb + i < a.Wo)
+                                sd[i] = acc[mg][i] + 128 * (sIi[i] + sT) - 16384 * K;
+                    }
+                }
             }
-        }
-
-        v4i acc[4];
+            // the lanes' writes are visible to the whole wavefront past here
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // lane l writes template 4s + l/16, positions 4*(l%16) .. +3
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) acc[nb] = (v4i){0, 0, 0, 0};
+            for (int s = 0; s < 4; s++) {
+                const int tl = 4 * s + (l >> 4), xq = 4 * (l & 15);
+                const float4 v = *(const float4 *)&ob[tl * OBP + xq];
+                const int tt = (g0 + bz * NB + nb) * 16 + tl;
+                if (!FULLT && tt >= a.nTpl) continue;
+                float *dst = a.coef + (size_t)tt * plane + orow + xq;
+                if (whole) {
+                    *(f4u *)dst = (f4u){v.x, v.y, v.z, v.w};
+                } else {
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ks++)
-#pragma unroll
-            for (int nb = 0; nb < 4; nb++)
-                if (nb < nblk)
-                    acc[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[ks], bop[nb][ks], acc[nb], 0, 0, 0);
-
-#pragma unroll
-        for (int nb = 0; nb < 4; nb++) {
-            if (nb >= nblk) break;
-            const int tt = (gbase + nb) * 16 + m;
-            if (tt >= a.nTpl) continue;
-            float gv[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int num = (int)((unsigned)K * (unsigned)acc[nb][i] +
-                                      (unsigned)sumIi[i] * (unsigned)ca[nb] + (unsigned)cb[nb]);
-                const float gm = (float)num * (rIi[i] * rT[nb]);
-                gv[i] = __builtin_amdgcn_fmed3f(gm, -1.0f, 1.0f);
+                    for (int i = 0; i < 4; i++)
+                        if (x0 + xq + i < a.Wo) dst[i] = vv[i];
+                }
             }
-            float *dst = a.coef + (size_t)tt * plane + orow + xb;
-            if (xb + 3 < a.Wo) {
-                f4u vv = {gv[0], gv[1], gv[2], gv[3]};
-                __builtin_nontemporal_store(vv, (f4u *)dst);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    if (xb + i < a.Wo) __builtin_nontemporal_store(gv[i], dst + i);
-            }
-            if (a.sums) {
-                int32_t *sd = a.sums + (size_t)(2 + tt) * plane + orow + xb;
-                const TStat ts = a.stats[tt];
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    if (xb + i < a.Wo)
-                        __builtin_nontemporal_store(
-                            (int)(acc[nb][i] + 128 * (sumIi[i] + (int)ts.sumT) - 16384 * K), sd + i);
-            }
+            // reads done before the buffer is written again
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 }
@@ -220,11 +275,47 @@ void bank_geometry(int wT, int hT, int *pitch, int *rowsT) {
     *rowsT = BY + hT - 1;
 }
 
+template <int KS, int NB>
+hipError_t launch_bank_nb(const CorrArgs &a, int g0, int nz, bool fullt, int nb16, int pitch,
+                          int rowsT, size_t lds, hipStream_t st) {
+    const int ntx = (a.Wo + BX - 1) / BX, nty = (a.Ho + BY - 1) / BY;
+    const int ntiles = ntx * nty * nz;
+    dim3 grid((ntiles + 7) / 8 * 8);
+    if (fullt)
+        hipLaunchKernelGGL((corr_bank<KS, NB, true>), grid, dim3(256), lds, st, a, nb16, pitch,
+                           rowsT, g0, ntx, nty, nz);
+    else
+        hipLaunchKernelGGL((corr_bank<KS, NB, false>), grid, dim3(256), lds, st, a, nb16, pitch,
+                           rowsT, g0, ntx, nty, nz);
+    return hipGetLastError();
+}
+
+template <int KS>
+hipError_t launch_bank_ks(const CorrArgs &a, int nb16, int pitch, int rowsT, size_t lds,
+                          hipStream_t st) {
+    // groups of 16 templates: blocks of 4 groups per workgroup, then the rest
+    const int ng = (a.nTpl + 15) / 16;
+    const bool tail16 = (a.nTpl % 16) != 0;
+    const int n4 = ng / 4, rest = ng % 4;
+    hipError_t e = hipSuccess;
+    if (n4 > 0) {
+        // the last group of the last full block may be partial
+        const bool fullt = !(tail16 && rest == 0);
+        e = launch_bank_nb<KS, 4>(a, 0, n4, fullt, nb16, pitch, rowsT, lds, st);
+        if (e != hipSuccess) return e;
+    }
+    const int g0 = 4 * n4;
+    if (rest == 1) e = launch_bank_nb<KS, 1>(a, g0, 1, !tail16, nb16, pitch, rowsT, lds, st);
+    if (rest == 2) e = launch_bank_nb<KS, 2>(a, g0, 1, !tail16, nb16, pitch, rowsT, lds, st);
+    if (rest == 3) e = launch_bank_nb<KS, 3>(a, g0, 1, !tail16, nb16, pitch, rowsT, lds, st);
+    return e;
+}
+
 }  // namespace
 
 bool corr_bank_supported(int wT, int hT, int nTpl) {
     const int chunks = hT * ((wT + 15) / 16);
-    return nTpl > 1 && chunks <= 16 && wT * hT <= 256;
+    return nTpl > 1 && hT <= 16 && chunks <= 16 && wT * hT <= 256;
 }
 
 hipError_t corr_bank_launch(const CorrArgs &a, hipStream_t st) {
@@ -233,27 +324,13 @@ hipError_t corr_bank_launch(const CorrArgs &a, hipStream_t st) {
     int pitch, rowsT;
     bank_geometry(a.wT, a.hT, &pitch, &rowsT);
     const size_t lds = (size_t)pitch * rowsT;
-    const bool full = (a.wT % 16 == 0) && ((a.hT * nb16) % 4 == 0);
-    dim3 grid((a.Wo + BX - 1) / BX, (a.Ho + BY - 1) / BY, ((a.nTpl + 15) / 16 + 3) / 4);
-#define NCC_BANK_CASE(KS)                                                                    \
-    case KS:                                                                                 \
-        if (full)                                                                            \
-            hipLaunchKernelGGL((corr_bank<KS, true>), grid, dim3(256), lds, st, a, nb16, pitch, \
-                               rowsT);                                                       \
-        else                                                                                 \
-            hipLaunchKernelGGL((corr_bank<KS, false>), grid, dim3(256), lds, st, a, nb16,    \
-                               pitch, rowsT);                                                \
-        break;
     switch (ks) {
-        NCC_BANK_CASE(1)
-        NCC_BANK_CASE(2)
-        NCC_BANK_CASE(3)
-        NCC_BANK_CASE(4)
-        default:
-            return hipErrorNotSupported;
+        case 1: return launch_bank_ks<1>(a, nb16, pitch, rowsT, lds, st);
+        case 2: return launch_bank_ks<2>(a, nb16, pitch, rowsT, lds, st);
+        case 3: return launch_bank_ks<3>(a, nb16, pitch, rowsT, lds, st);
+        case 4: return launch_bank_ks<4>(a, nb16, pitch, rowsT, lds, st);
+        default: return hipErrorNotSupported;
     }
-#undef NCC_BANK_CASE
-    return hipGetLastError();
 }
 
 }  // namespace ncc
