@@ -113,6 +113,49 @@ def cpu_baseline(img, tpl, budget_s=12.0):
     }
 
 
+def run_loop(args, L, sh, d):
+    """Repeats one call type; the workload of each is the one the JSON line
+    reports for it."""
+    import torch
+    from normalized_cross_correlation_amd import synth
+    if args.loop == "copy":
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=d)
+        dst = torch.empty_like(src)
+        fns = [lambda: dst.copy_(src)]
+    else:
+        name = {"sat": "sat", "box": "sat", "corr": "headline", "bank": "bank"}[args.loop]
+        w = synth.make(name)
+        img = torch.from_numpy(w["img"]).to(d)
+        H, W = img.shape
+        S = torch.empty((H, W), dtype=torch.int64, device=d)
+        Q = torch.empty_like(S)
+        if args.loop in ("sat", "box"):
+            rects = torch.from_numpy(w["rects"]).to(d)
+            n = rects.shape[0]
+            out = torch.empty((n,), dtype=torch.int64, device=d)
+            assert L.ncc_sat_build(img.data_ptr(), W, H, S.data_ptr(), Q.data_ptr(), sh) == 0
+            if args.loop == "sat":
+                fns = [lambda: L.ncc_sat_build(img.data_ptr(), W, H, S.data_ptr(), Q.data_ptr(), sh)]
+            else:
+                fns = [lambda: L.ncc_box(S.data_ptr(), W, H, rects.data_ptr(), n, out.data_ptr(), sh)]
+        else:
+            tpl = torch.from_numpy(w["tpl"]).to(d)
+            nt, hT, wT = tpl.shape
+            coef = torch.empty((nt, H - hT + 1, W - wT + 1), dtype=torch.float32, device=d)
+            fns = [lambda: L.ncc_correlate(img.data_ptr(), W, H, tpl.data_ptr(), wT, hT, nt, None,
+                                           coef.data_ptr(), sh)]
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    for _ in range(args.steps):
+        for f in fns:
+            rc = f()
+            if isinstance(rc, int) and rc != 0:
+                raise RuntimeError("%s loop call failed: %d" % (args.loop, rc))
+    torch.cuda.synchronize()
+    print("loop %s: %d calls done" % (args.loop, args.steps), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +164,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="time only the headline step (used under the profiler)")
+    ap.add_argument("--loop", choices=["sat", "corr", "bank", "box", "copy"],
+                    help="profiling aid: run one call type --steps times after --warmup and "
+                         "exit without the JSON line (copy: a plain 256 MiB device copy, the "
+                         "reference for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -137,6 +184,9 @@ def main():
     stream = torch.cuda.current_stream(d)
     L = ncc.lib()
     sh = stream.cuda_stream
+    if args.loop:
+        run_loop(args, L, sh, d)
+        return
 
     # ---------------------------------------------------------- headline --
     w = synth.make("headline")

@@ -58,13 +58,10 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
     __shared__ int sIs[BY][BX];         // SumI per position
     __shared__ float rIs[BY][BX];       // 1/sqrt(varI) per position, 0 if varI == 0
     __shared__ float obuf[4][16][OBP];  // per wavefront: 16 templates x 64 positions
-    // Workgroups go to the 8 XCDs round-robin in launch order; tile k/8 of
-    // XCD k%8's contiguous range keeps each XCD's L2 writing one compact
-    // stretch of the output maps (several times the write bandwidth of
-    // interleaved tiles).
-    const int ntiles = ntx * nty * nz, per = (ntiles + 7) / 8;
-    const int tix = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (tix >= ntiles) return;
+    // XCD-contiguous tile order: several times the write bandwidth of tiles
+    // interleaved across the XCDs' L2s for these 64-template output maps
+    const int tix = xcd_tile((int)blockIdx.x, ntx * nty * nz);
+    if (tix < 0) return;
     const int bz = tix / (ntx * nty), bxy = tix % (ntx * nty);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int g = l >> 4, m = l & 15;
@@ -279,8 +276,7 @@ template <int KS, int NB>
 hipError_t launch_bank_nb(const CorrArgs &a, int g0, int nz, bool fullt, int nb16, int pitch,
                           int rowsT, size_t lds, hipStream_t st) {
     const int ntx = (a.Wo + BX - 1) / BX, nty = (a.Ho + BY - 1) / BY;
-    const int ntiles = ntx * nty * nz;
-    dim3 grid((ntiles + 7) / 8 * 8);
+    dim3 grid(xcd_grid(ntx * nty * nz));
     if (fullt)
         hipLaunchKernelGGL((corr_bank<KS, NB, true>), grid, dim3(256), lds, st, a, nb16, pitch,
                            rowsT, g0, ntx, nty, nz);

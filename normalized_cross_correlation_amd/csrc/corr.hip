@@ -226,7 +226,7 @@ __device__ __forceinline__ void stream_rows(StreamState<WT4, HT, POS> &st, const
 }
 
 template <int WT4, int HT, int POS, int WAVES, int RS, int ALIGN, bool TALIGN>
-__global__ __launch_bounds__(WAVES * 64) void corr_stream(CorrArgs a, int t) {
+__global__ __launch_bounds__(WAVES * 64) void corr_stream(CorrArgs a, int t, int ntx, int nty) {
     static_assert(RS % HT == 0, "strip height must be whole batches");
     static_assert(POS == 1 || POS == 2, "one or two columns per lane");
     constexpr int NT = WAVES * 64;                     // lanes per workgroup
@@ -237,8 +237,10 @@ __global__ __launch_bounds__(WAVES * 64) void corr_stream(CorrArgs a, int t) {
     constexpr int LOADS = (HT * CH + NT - 1) / NT;     // chunk loads per thread per batch
     __shared__ uint32_t buf[2][HT][PITCH];
 
+    const int tix = xcd_tile((int)blockIdx.x, ntx * nty);
+    if (tix < 0) return;
     const int tid = threadIdx.x;
-    const int x0 = blockIdx.x * NC, y0 = blockIdx.y * RS;
+    const int x0 = (tix % ntx) * NC, y0 = (tix / ntx) * RS;
     const int rowsOut = min(RS, a.Ho - y0);
 
     StreamState<WT4, HT, POS> st;
@@ -493,16 +495,17 @@ constexpr int STREAM_POS = NCC_STREAM_POS;      // output columns per lane
 template <int WT4, int HT, bool TALIGN>
 hipError_t launch_stream_t(const CorrArgs &a, int t, hipStream_t st) {
     constexpr int NC = STREAM_WAVES * 64 * STREAM_POS;
-    dim3 grid((a.Wo + NC - 1) / NC, (a.Ho + STREAM_RS - 1) / STREAM_RS), block(STREAM_WAVES * 64);
+    const int ntx = (a.Wo + NC - 1) / NC, nty = (a.Ho + STREAM_RS - 1) / STREAM_RS;
+    dim3 grid(xcd_grid(ntx * nty)), block(STREAM_WAVES * 64);
     if (a.W % 16 == 0 && ((uintptr_t)a.img & 15) == 0)
         hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, STREAM_RS, 16, TALIGN>),
-                           grid, block, 0, st, a, t);
+                           grid, block, 0, st, a, t, ntx, nty);
     else if (a.W % 4 == 0 && ((uintptr_t)a.img & 3) == 0)
         hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, STREAM_RS, 4, TALIGN>),
-                           grid, block, 0, st, a, t);
+                           grid, block, 0, st, a, t, ntx, nty);
     else
         hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, STREAM_RS, 1, TALIGN>),
-                           grid, block, 0, st, a, t);
+                           grid, block, 0, st, a, t, ntx, nty);
     return hipGetLastError();
 }
 

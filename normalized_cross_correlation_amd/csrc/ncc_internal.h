@@ -133,6 +133,21 @@ NCC_DEV uint32_t wave_sum_u32(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_u32(x), 63);
 }
 
+// Workgroups are handed to the 8 XCDs of the chip round-robin in launch
+// order.  Launching ceil(ntiles/8)*8 workgroups and mapping launch index k to
+// tile (k % 8) * ceil(ntiles/8) + k / 8 gives each XCD one contiguous run of
+// tiles, so each XCD's L2 writes back one compact stretch of the output;
+// indices past ntiles (returned as -1) do nothing.
+constexpr int NUM_XCD = 8;
+NCC_DEV int xcd_tile(int k, int ntiles) {
+    const int per = (ntiles + NUM_XCD - 1) / NUM_XCD;
+    const int t = (k % NUM_XCD) * per + k / NUM_XCD;
+    return t < ntiles ? t : -1;
+}
+inline unsigned xcd_grid(int ntiles) {
+    return (unsigned)((ntiles + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
+}
+
 NCC_DEV uint32_t dot4u(uint32_t a, uint32_t b, uint32_t c) {
     return __builtin_amdgcn_udot4(a, b, c, false);
 }

@@ -274,7 +274,9 @@ template <bool VEC>
 __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__ img, int W, int H,
                                                      SatWork wk, int64_t *__restrict__ S,
                                                      int64_t *__restrict__ Q) {
-    const int s = blockIdx.x, b = blockIdx.y;
+    const int tix = xcd_tile((int)blockIdx.x, wk.nStrips * wk.nBands);
+    if (tix < 0) return;
+    const int s = tix % wk.nStrips, b = tix / wk.nStrips;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int x = s * SAT_SW + 2 * l;
     const int y0 = b * SAT_BH + w * WAVE_ROWS;
@@ -424,7 +426,7 @@ hipError_t sat_build_launch(const uint8_t *img, int W, int H, int64_t *S, int64_
                        nCpBlocks, nRowBlocks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid(wk.nStrips, wk.nBands);
+    dim3 grid(xcd_grid(wk.nStrips * wk.nBands));
     if (dvec)
         hipLaunchKernelGGL(sat_downsweep<true>, grid, block, 0, st, img, W, H, wk, S, Q);
     else
