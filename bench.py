@@ -227,7 +227,7 @@ def main():
     comp = {
         "ncc_sat_build": {"ms": round(t_sat, 5), "GB/s": round(sat_rate, 1),
                           "frac_hbm": round(sat_rate / HBM_PEAK_GBS, 4),
-                          "kernels": "sat_reduce, sat_carry, sat_downsweep"},
+                          "kernels": "sat_rows, sat_top, sat_downsweep"},
         "ncc_correlate": {"ms": round(t_corr, 5), "Gcoeff/s": round(coeffs / (t_corr * 1e-3) / 1e9, 1),
                           "TOP/s": round(corr_rate, 2), "frac_dot4": round(corr_rate / DOT4_PEAK_TOPS, 4),
                           "kernels": "corr_stream<4,16>"},
@@ -238,7 +238,7 @@ def main():
                 "frac": round(corr_rate / DOT4_PEAK_TOPS, 4),
                 "traffic": _traffic("corr_stream_headline", ["corr.hip", "ncc_internal.h"])}
     else:
-        roof = {"kernel": "ncc_sat_build (sat_reduce + sat_carry + sat_downsweep)", "bound": "hbm",
+        roof = {"kernel": "ncc_sat_build (sat_rows + sat_top + sat_downsweep)", "bound": "hbm",
                 "achieved": round(sat_rate, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(sat_rate / HBM_PEAK_GBS, 4),
                 "traffic": _traffic("sat_build_headline", ["sat.hip", "ncc_internal.h"])}

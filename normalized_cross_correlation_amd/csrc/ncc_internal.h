@@ -9,20 +9,23 @@
 namespace ncc {
 
 // ---------------------------------------------------------------- tables ---
-// Table build tiling: a workgroup of 4 wavefronts owns a tile of
-// SAT_SW columns x SAT_BH rows; each lane owns 2 adjacent columns and each
-// wavefront 16 rows of the tile.
+// Table build tiling: the row pass takes bands of SAT_BH rows across
+// segments of SAT_QW columns; the downsweep takes tiles of SAT_SW columns x
+// SAT_SUB bands, a lane owning 2 adjacent columns and each of the 4
+// wavefronts SAT_BH / 4 rows of every band.
 constexpr int SAT_SW = 128;
-constexpr int SAT_BH = 64;
+constexpr int SAT_BH = 32;
+constexpr int SAT_QW = 1024;
+constexpr int SAT_SUB = 4;
 
 struct SatWork {
-    int nStrips, nBands;
-    uint32_t *colsum;   // [2][nBands][W]    column sums of each band
-    uint32_t *rowtot;   // [2][H][nStrips]   row sums of each strip
-    uint64_t *tiletot;  // [2][nBands][nStrips]
-    uint64_t *cp;       // [2][nBands][W]    column sums of all rows above the band
-    uint32_t *lrow;     // [2][H][nStrips]   row sums of all columns left of the strip
-    int64_t *corner;    // [2][nBands][nStrips] table value above-left of the tile
+    int nStrips, nBands, nSeg;
+    uint32_t *lrowl;    // [2][H][nStrips] row sum of the segment's strips left of each strip
+    uint32_t *segtot;   // [2][H][nSeg]    row sum of each segment
+    uint32_t *bandcol;  // [2][nBands][W]  band sum of the segment-local row running sums
+    uint32_t *bandseg;  // [2][nBands][nSeg] band total of each segment
+    uint64_t *top;      // [2][ceil(nBands/SAT_SUB)][W] table value on the row above
+                        //   each downsweep tile row
 };
 
 size_t sat_work_bytes(int W, int H);
