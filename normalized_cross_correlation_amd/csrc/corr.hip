@@ -71,8 +71,10 @@ struct StreamState {
     uint32_t sh[POS];          // byte offset of each window in the lane's first dword
     uint32_t mlast, K, sumT;
     float varTf;
-    float *out;                // the lane's first coefficient in the next finished row
-    int32_t *s0, *s1, *s2;     // its sums
+    float *out;                // the strip's first output row (workgroup-uniform) ...
+    int32_t *s0, *s1, *s2;     // ... and its sums planes
+    uint32_t off;              // + this offset (elements): the lane's first column of the
+                               //   next finished row
     bool wsum, wfirst;         // sums wanted; SumI / SumISq planes written by this call
     bool pairs;                // wave-uniform: every lane's POS columns are distinct
     int yrel;                  // output row (relative to the strip) finished next
@@ -172,38 +174,36 @@ __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
 #pragma unroll
         for (int p = 0; p < POS; p++) g[p] = stream_coef(st, sumI[p], sumISq[p], sumIT[p]);
         if (POS == 2 && st.pairs) {
-            __builtin_nontemporal_store((f2u){g[0], g[POS - 1]}, (f2u *)st.out);
+            __builtin_nontemporal_store((f2u){g[0], g[POS - 1]}, (f2u *)(st.out + st.off));
             if (st.wsum) {
                 if (st.wfirst) {
-                    __builtin_nontemporal_store((i2u){(int)sumI[0], (int)sumI[POS - 1]}, (i2u *)st.s0);
+                    __builtin_nontemporal_store((i2u){(int)sumI[0], (int)sumI[POS - 1]},
+                                                (i2u *)(st.s0 + st.off));
                     __builtin_nontemporal_store((i2u){(int)sumISq[0], (int)sumISq[POS - 1]},
-                                                (i2u *)st.s1);
+                                                (i2u *)(st.s1 + st.off));
                 }
-                __builtin_nontemporal_store((i2u){(int)sumIT[0], (int)sumIT[POS - 1]}, (i2u *)st.s2);
+                __builtin_nontemporal_store((i2u){(int)sumIT[0], (int)sumIT[POS - 1]},
+                                            (i2u *)(st.s2 + st.off));
             }
         } else {
             // edge lanes: column p of this lane is min(first + p, Wo - 1)
 #pragma unroll
             for (int p = 0; p < POS; p++) {
                 const int dp = (int)(st.sh[p] - st.sh[0]);
-                store_coef(st.out + dp, g[p]);
+                const uint32_t o = st.off + dp;
+                store_coef(st.out + o, g[p]);
                 if (st.wsum) {
                     if (st.wfirst) {
-                        store_sum(st.s0 + dp, (int32_t)sumI[p]);
-                        store_sum(st.s1 + dp, (int32_t)sumISq[p]);
+                        store_sum(st.s0 + o, (int32_t)sumI[p]);
+                        store_sum(st.s1 + o, (int32_t)sumISq[p]);
                     }
-                    store_sum(st.s2 + dp, (int32_t)sumIT[p]);
+                    store_sum(st.s2 + o, (int32_t)sumIT[p]);
                 }
             }
         }
     }
     st.yrel++;
-    st.out += Wo;
-    if (st.wsum) {
-        st.s0 += Wo;
-        st.s1 += Wo;
-        st.s2 += Wo;
-    }
+    st.off += Wo;
 }
 
 // Rows Q .. HT-1 of a batch; the LDS reads of row Q+1 are issued before row
@@ -226,7 +226,11 @@ __device__ __forceinline__ void stream_rows(StreamState<WT4, HT, POS> &st, const
 }
 
 template <int WT4, int HT, int POS, int WAVES, int RS, int ALIGN, bool TALIGN>
-__global__ __launch_bounds__(WAVES * 64) void corr_stream(CorrArgs a, int t, int ntx, int nty) {
+#ifndef NCC_STREAM_WPE
+#define NCC_STREAM_WPE 3
+#endif
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(NCC_STREAM_WPE)))
+void corr_stream(CorrArgs a, int t, int ntx, int nty) {
     static_assert(RS % HT == 0, "strip height must be whole batches");
     static_assert(POS == 1 || POS == 2, "one or two columns per lane");
     constexpr int NT = WAVES * 64;                     // lanes per workgroup
@@ -291,7 +295,9 @@ __global__ __launch_bounds__(WAVES * 64) void corr_stream(CorrArgs a, int t, int
     }
     st.yrel = 0;
     const size_t plane = (size_t)a.Ho * a.Wo;
-    const size_t o0 = (size_t)y0 * a.Wo + xa;
+    // per-strip bases keep the per-lane offset within 32 bits
+    const size_t o0 = (size_t)y0 * a.Wo;
+    st.off = (uint32_t)xa;
     st.out = a.coef + (size_t)t * plane + o0;
     st.wsum = a.sums != nullptr;
     st.wfirst = t == 0;
@@ -307,6 +313,21 @@ __global__ __launch_bounds__(WAVES * 64) void corr_stream(CorrArgs a, int t, int
     uint4 pre[LOADS];
     const bool colsIn = ALIGN == 16 && x0 + 16 * CH <= a.W;
     auto fetch = [&](int bt) {
+        if (ALIGN == 16) {
+            // W % 16 == 0: a chunk lies wholly inside or wholly outside the
+            // image; load from a clamped in-bounds address and zero what lies
+            // outside (a select, not a branch)
+#pragma unroll
+            for (int u = 0; u < LOADS; u++) {
+                const int i = tid + u * NT;
+                const int r = i / CH, c = i % CH;
+                const int y = y0 + bt * HT + r, x = x0 + 16 * c;
+                const uint4 v = *(const uint4 *)(a.img + (size_t)min(y, a.H - 1) * a.W + min(x, a.W - 16));
+                const bool ok = i < HT * CH && y < a.H && x < a.W;
+                pre[u] = ok ? v : make_uint4(0, 0, 0, 0);
+            }
+            return;
+        }
         const bool inside = colsIn && y0 + (bt + 1) * HT <= a.H;
         if (inside) {
 #pragma unroll
@@ -486,7 +507,7 @@ __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int
 #define NCC_STREAM_RS 64
 #endif
 #ifndef NCC_STREAM_POS
-#define NCC_STREAM_POS 2
+#define NCC_STREAM_POS 1
 #endif
 constexpr int STREAM_WAVES = NCC_STREAM_WAVES;  // wavefronts per workgroup
 constexpr int STREAM_RS = NCC_STREAM_RS;        // output rows per strip
