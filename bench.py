@@ -7,8 +7,11 @@ summed-area tables (ncc_sat_build: S and Q, int64) and correlate
 resident in device memory before timing starts.
 
 Printed: ONE JSON line.  `value` is coefficients per second of whole steps
-(Gcoeff/s).  `roofline` covers the step's dominant kernel, timed with HIP
-events around its calls inside the timed region.  Also reported, from the same
+(Gcoeff/s): K steps run back to back between two device synchronisations.
+`roofline` covers the step's dominant kernel; its duration comes from HIP
+events recorded around every call in a second pass of K steps (events between
+calls keep kernels from overlapping, so that pass is not used for the step
+rate).  Also reported, from the same
 run: the table build alone on 4096 x 4096 uniform bytes (GB/s of algorithmic
 traffic, 17 B per pixel) with 1 000 000 box queries, and the 64-template bank
 workload; and the CPU oracle timed on a bounded sample (cpu_baseline).
@@ -58,27 +61,39 @@ def _traffic(kernel_key, src_names):
     return t.get("bytes_per_launch")
 
 
-def time_calls(fns, steps, warmup, stream):
-    """Runs `steps` steps of the callables in `fns` (one step = each once, in
-    order) after `warmup` untimed steps.  Returns (wall seconds of the timed
-    steps, mean ms of each callable from HIP events on `stream`)."""
+def time_steps(fns, steps, warmup):
+    """Wall seconds of `steps` steps (one step = each callable once, in order,
+    back to back on the device) after `warmup` untimed steps, bracketed by a
+    device synchronisation on both sides."""
     import torch
     for _ in range(warmup):
         for f in fns:
             f()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
+    for _ in range(steps):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_each(fns, steps, stream):
+    """Mean ms of each callable from HIP events recorded on `stream` around
+    every call, over `steps` more steps.  An event between two calls makes
+    the second wait for the first to drain, so this pass times the calls, not
+    the step."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
     for s in range(steps):
         ev[s][0].record(stream)
         for i, f in enumerate(fns):
             f()
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
-           for i in range(len(fns))]
-    return wall, per
+    return [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+            for i in range(len(fns))]
 
 
 def cpu_baseline(img, tpl, budget_s=12.0):
@@ -211,8 +226,10 @@ def main():
         if rc:
             raise RuntimeError("ncc_correlate: %d" % rc)
 
-    wall, (t_sat, t_corr) = time_calls([sat, corr], args.steps, args.warmup, stream)
+    wall = time_steps([sat, corr], args.steps, args.warmup)
     ms_step = wall / args.steps * 1e3
+    # per-call durations (for the roofline and components) from a second pass
+    t_sat, t_corr = time_each([sat, corr], args.steps, stream)
     coeffs = Ho * Wo
     value = coeffs / (ms_step * 1e-3) / 1e9
 
@@ -282,7 +299,8 @@ def main():
             assert L.ncc_box(pS, W, H, pr, n, pb1, sh) == 0
             assert L.ncc_box(pQ, W, H, pr, n, pb2, sh) == 0
 
-        _, (t_b, t_q) = time_calls([sat2, boxes], 20, 3, stream)
+        time_steps([sat2, boxes], 0, 3)
+        t_b, t_q = time_each([sat2, boxes], 20, stream)
         rate = sat_bytes / (t_b * 1e-3) / 1e9
         out["sat_workload"] = {
             "workload": "4096x4096 u8 uniform: ncc_sat_build, then 1,000,000 box queries on S and on Q",
@@ -300,7 +318,8 @@ def main():
         def bank():
             assert L.ncc_correlate(pbi, W, H, pbt, wT, hT, nb, None, pbc, sh) == 0
 
-        _, (t_k,) = time_calls([bank], 10, 2, stream)
+        time_steps([bank], 0, 2)
+        t_k, = time_each([bank], 10, stream)
         bcoeffs = nb * coeffs
         out_bytes = bcoeffs * 4 + H * W
         bw = out_bytes / (t_k * 1e-3) / 1e9
