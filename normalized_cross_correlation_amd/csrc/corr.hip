@@ -92,17 +92,20 @@ __device__ __forceinline__ uint32_t to_vgpr(uint32_t x) {
 typedef float f2u __attribute__((ext_vector_type(2), aligned(4)));
 typedef int i2u __attribute__((ext_vector_type(2), aligned(4)));
 
+// nI = -SumI (mod 2^32), as the running sums give it.
 template <int WT4, int HT, int POS>
-__device__ __forceinline__ float stream_coef(const StreamState<WT4, HT, POS> &st, uint32_t sumI,
+__device__ __forceinline__ float stream_coef(const StreamState<WT4, HT, POS> &st, uint32_t nI,
                                              uint32_t sumISq, uint32_t sumIT) {
     if (HT * 4 * WT4 <= 256) {
-        // operands < 2^24 and |num| <= K^2 * 127.5^2 < 2^31: exact mod 2^32
-        const int32_t num = (int32_t)(__umul24(st.K, sumIT) - __umul24(sumI, st.sumT));
-        const uint32_t varI = __umul24(st.K, sumISq) - __umul24(sumI, sumI);
+        // K*SumIT < 2^24 and SumISq < 2^24 (unsigned 24-bit products); SumI,
+        // SumT < 2^16 (signed 24-bit); |num| <= K^2 * 127.5^2 < 2^31: exact mod 2^32
+        const int32_t num = __mul24((int)st.sumT, (int)nI) + (int32_t)__umul24(st.K, sumIT);
+        const uint32_t varI = __umul24(st.K, sumISq) - (uint32_t)__mul24((int)nI, (int)nI);
         return ncc_coef((float)num, (float)varI, st.varTf);
     } else {
-        const long long num = (long long)st.K * sumIT - (long long)sumI * st.sumT;
-        const long long varI = (long long)st.K * sumISq - (long long)sumI * sumI;
+        const long long sumI = -(long long)(int32_t)nI;
+        const long long num = (long long)st.K * sumIT - sumI * st.sumT;
+        const long long varI = (long long)st.K * sumISq - sumI * sumI;
         return ncc_coef((float)num, (float)varI, st.varTf);
     }
 }
@@ -156,12 +159,12 @@ __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
     // nor may later rows' loads and byte shifts be hoisted into this one
     __builtin_amdgcn_sched_barrier(0);
     constexpr int fin = (Q + 1) % HT;
-    uint32_t sumIT[POS], sumI[POS], sumISq[POS];
+    uint32_t sumIT[POS], nI[POS], sumISq[POS];
 #pragma unroll
     for (int p = 0; p < POS; p++) {
         sumIT[p] = st.acc[p][fin];
         st.acc[p][fin] = 0;
-        sumI[p] = st.PI[p] - st.pI[p][Q];
+        nI[p] = st.pI[p][Q] - st.PI[p];
         sumISq[p] = st.PQ[p] - st.pQ[p][Q];
         st.pI[p][Q] = st.PI[p];
         st.pQ[p][Q] = st.PQ[p];
@@ -172,12 +175,12 @@ __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
     if (st.yrel < rowsOut) {
         float g[POS];
 #pragma unroll
-        for (int p = 0; p < POS; p++) g[p] = stream_coef(st, sumI[p], sumISq[p], sumIT[p]);
+        for (int p = 0; p < POS; p++) g[p] = stream_coef(st, nI[p], sumISq[p], sumIT[p]);
         if (POS == 2 && st.pairs) {
             __builtin_nontemporal_store((f2u){g[0], g[POS - 1]}, (f2u *)(st.out + st.off));
             if (st.wsum) {
                 if (st.wfirst) {
-                    __builtin_nontemporal_store((i2u){(int)sumI[0], (int)sumI[POS - 1]},
+                    __builtin_nontemporal_store((i2u){-(int)nI[0], -(int)nI[POS - 1]},
                                                 (i2u *)(st.s0 + st.off));
                     __builtin_nontemporal_store((i2u){(int)sumISq[0], (int)sumISq[POS - 1]},
                                                 (i2u *)(st.s1 + st.off));
@@ -194,7 +197,7 @@ __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
                 store_coef(st.out + o, g[p]);
                 if (st.wsum) {
                     if (st.wfirst) {
-                        store_sum(st.s0 + o, (int32_t)sumI[p]);
+                        store_sum(st.s0 + o, -(int32_t)nI[p]);
                         store_sum(st.s1 + o, (int32_t)sumISq[p]);
                     }
                     store_sum(st.s2 + o, (int32_t)sumIT[p]);

@@ -167,12 +167,13 @@ NCC_DEV uint32_t byte_mask(int nb) {
 
 // The coefficient from exact integer numerator and window variance and the
 // template's variance as float.  A zero variance yields 0: varI == 0 forces
-// num == 0 (every window pixel equal), varT == 0 likewise, so clamping the
-// product to >= 1 only guards 0 * inf.
+// num == 0 (every window pixel equal), varT == 0 likewise.  For nonzero
+// integer variances the product is >= 1 and 1/sqrt of it <= 1, so clamping
+// 1/sqrt to [0, 1] (the instruction's clamp modifier) changes nothing but
+// turns 1/sqrt(0) = inf into 1, and 0 * 1 = 0.
 NCC_DEV float ncc_coef(float numf, float varIf, float varTf) {
-    float p = fmaxf(varIf * varTf, 1.0f);
-    float g = numf * __builtin_amdgcn_rsqf(p);
-    return __builtin_amdgcn_fmed3f(g, -1.0f, 1.0f);
+    const float r = __builtin_amdgcn_fmed3f(__builtin_amdgcn_rsqf(varIf * varTf), 0.0f, 1.0f);
+    return __builtin_amdgcn_fmed3f(numf * r, -1.0f, 1.0f);
 }
 
 }  // namespace ncc
