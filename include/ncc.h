@@ -117,8 +117,10 @@ int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n,
  * Errors: NCC_EINVAL (null img/tpl/coef_out, W or H < 1, wT or hT < 1,
  * wT > W, hT > H, nTpl < 1), NCC_ERANGE (W > NCC_MAX_WIDTH,
  * wT*hT > NCC_MAX_TEMPLATE_PIXELS, outputs past 2^62 bytes),
- * NCC_EUNSUPPORTED (a template whose staged image tile does not fit the
- * 160 KiB of LDS of one workgroup), NCC_ENOMEM, NCC_EHIP.
+ * NCC_EUNSUPPORTED (called during stream capture before the stream's
+ * workspace was sized by an uncaptured call), NCC_ENOMEM, NCC_EHIP.  Every
+ * template shape within the bounds above is supported: templates whose
+ * staged image tile exceeds the LDS of one workgroup run in blocks.
  */
 int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl,
                   int wT, int hT, int nTpl, int32_t *sums_out,

@@ -25,7 +25,8 @@
 //
 // corr_generic (any shape): 64 x 64 output tile per workgroup, 4 x 4 outputs
 // per lane, dot4 over an LDS-staged tile + halo; SumI and SumISq by satBox on
-// the full int64 tables.
+// the full int64 tables.  A template whose tile + halo exceeds the LDS is
+// taken in blocks of rows x dwords, each block staging its part of the image.
 #include "ncc_internal.h"
 
 namespace ncc {
@@ -421,28 +422,12 @@ __device__ __forceinline__ long long sat_box(const int64_t *S, int W, int x0, in
 
 __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int64_t *__restrict__ S,
                                                     const int64_t *__restrict__ Q, int pitch,
-                                                    int rowsT) {
+                                                    int rowsT, int jb, int kb) {
     extern __shared__ uint32_t tile[];  // rowsT x pitch bytes
     const int tid = threadIdx.x;
     const int x0 = blockIdx.x * GT, y0 = blockIdx.y * GT;
     const int wt4 = (a.wT + 3) / 4;
     const int pw = pitch / 4;
-
-    // stage the tile + halo
-    for (int i = tid; i < rowsT * pw; i += 256) {
-        const int r = i / pw, c = i % pw;
-        const int y = y0 + r, xb = x0 + 4 * c;
-        uint32_t v = 0;
-        if (y < a.H) {
-            const uint8_t *row = a.img + (size_t)y * a.W;
-#pragma unroll
-            for (int b = 0; b < 4; b++)
-                if (xb + b < a.W) v |= (uint32_t)row[xb + b] << (8 * b);
-        }
-        tile[i] = v;
-    }
-    __syncthreads();
-
     const int tx = tid & 15, ty = tid >> 4;
     uint32_t acc[4][4];
 #pragma unroll
@@ -451,25 +436,50 @@ __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int
         for (int s = 0; s < 4; s++) acc[dy][s] = 0;
     const uint32_t *trow = a.rows + (size_t)t * a.hT * wt4;
 
-    for (int r = 0; r < a.hT + 3; r++) {
-        const uint32_t *rowp = tile + (4 * ty + r) * pw + tx;
-        uint32_t lo = rowp[0];
-        for (int k = 0; k < wt4; k++) {
-            const uint32_t hi = rowp[k + 1];
-            const uint32_t v0 = lo, v1 = align_bytes(hi, lo, 1), v2 = align_bytes(hi, lo, 2),
-                           v3 = align_bytes(hi, lo, 3);
+    // the template in blocks of jb rows x kb dwords (one block when the whole
+    // tile + halo fits in LDS); each block stages its part of the image
+    for (int j0 = 0; j0 < a.hT; j0 += jb) {
+        const int j1 = min(j0 + jb, a.hT);
+        for (int k0 = 0; k0 < wt4; k0 += kb) {
+            const int k1 = min(k0 + kb, wt4);
+            const int rowsB = GT + (j1 - j0) + 2;  // staged rows of this block
+            __syncthreads();  // the previous block's reads are done
+            for (int i = tid; i < rowsB * pw; i += 256) {
+                const int r = i / pw, c = i % pw;
+                const int y = y0 + j0 + r, xb = x0 + 4 * (k0 + c);
+                uint32_t v = 0;
+                if (y < a.H) {
+                    const uint8_t *row = a.img + (size_t)y * a.W;
 #pragma unroll
-            for (int dy = 0; dy < 4; dy++) {
-                const int j = r - dy;
-                if (j >= 0 && j < a.hT) {
-                    const uint32_t tv = trow[j * wt4 + k];
-                    acc[dy][0] = dot4u(v0, tv, acc[dy][0]);
-                    acc[dy][1] = dot4u(v1, tv, acc[dy][1]);
-                    acc[dy][2] = dot4u(v2, tv, acc[dy][2]);
-                    acc[dy][3] = dot4u(v3, tv, acc[dy][3]);
+                    for (int bb = 0; bb < 4; bb++)
+                        if (xb + bb < a.W) v |= (uint32_t)row[xb + bb] << (8 * bb);
+                }
+                tile[i] = v;
+            }
+            __syncthreads();
+            // staged row r is image row y0 + j0 + r; output row 4ty + dy meets
+            // template row j = j0 + r - 4ty - dy
+            for (int r = 0; r < (j1 - j0) + 3; r++) {
+                const uint32_t *rowp = tile + (4 * ty + r) * pw + tx;
+                uint32_t lo = rowp[0];
+                for (int k = k0; k < k1; k++) {
+                    const uint32_t hi = rowp[k - k0 + 1];
+                    const uint32_t v0 = lo, v1 = align_bytes(hi, lo, 1), v2 = align_bytes(hi, lo, 2),
+                                   v3 = align_bytes(hi, lo, 3);
+#pragma unroll
+                    for (int dy = 0; dy < 4; dy++) {
+                        const int j = j0 + r - dy;
+                        if (j >= j0 && j < j1) {
+                            const uint32_t tv = trow[j * wt4 + k];
+                            acc[dy][0] = dot4u(v0, tv, acc[dy][0]);
+                            acc[dy][1] = dot4u(v1, tv, acc[dy][1]);
+                            acc[dy][2] = dot4u(v2, tv, acc[dy][2]);
+                            acc[dy][3] = dot4u(v3, tv, acc[dy][3]);
+                        }
+                    }
+                    lo = hi;
                 }
             }
-            lo = hi;
         }
     }
 
@@ -541,10 +551,24 @@ hipError_t launch_stream(const CorrArgs &a, int t, hipStream_t st) {
     return launch_stream_t<WT4, HT, false>(a, t, st);
 }
 
-void generic_geometry(int wT, int hT, int *pitch, int *rowsT) {
+// Template blocking of the generic kernel: the whole template when its tile +
+// halo fits the LDS budget, else blocks of GEN_JB rows x GEN_KB dwords.
+constexpr size_t GEN_LDS = 160 * 1024;
+constexpr int GEN_JB = 64, GEN_KB = 128;
+
+void generic_geometry(int wT, int hT, int *pitch, int *rowsT, int *jb, int *kb) {
     const int wt4 = (wT + 3) / 4;
-    *pitch = ((GT + 4 * wt4 + 4) + 15) / 16 * 16;
-    *rowsT = GT + hT + 2;
+    *jb = hT;
+    *kb = wt4;
+    auto fits = [&]() {
+        *pitch = ((GT + 4 * *kb + 4) + 15) / 16 * 16;
+        *rowsT = GT + *jb + 2;
+        return (size_t)*pitch * *rowsT <= GEN_LDS;
+    };
+    if (fits()) return;
+    *jb = hT < GEN_JB ? hT : GEN_JB;
+    *kb = wt4 < GEN_KB ? wt4 : GEN_KB;
+    fits();  // at most 592 x 130 bytes (77 KB)
 }
 
 }  // namespace
@@ -559,26 +583,24 @@ hipError_t corr_stream_launch(const CorrArgs &a, int t, hipStream_t st) {
 }
 
 bool corr_generic_supported(int wT, int hT) {
-    int pitch, rowsT;
-    generic_geometry(wT, hT, &pitch, &rowsT);
-    return (size_t)pitch * rowsT <= 160 * 1024;
+    return wT >= 1 && hT >= 1;  // any shape: large templates run in blocks
 }
 
 hipError_t corr_generic_launch(const CorrArgs &a, int t, const int64_t *S, const int64_t *Q,
                                hipStream_t st) {
-    int pitch, rowsT;
-    generic_geometry(a.wT, a.hT, &pitch, &rowsT);
+    int pitch, rowsT, jb, kb;
+    generic_geometry(a.wT, a.hT, &pitch, &rowsT, &jb, &kb);
     size_t lds = (size_t)pitch * rowsT;
-    if (lds > 160 * 1024) return hipErrorNotSupported;
+    if (lds > GEN_LDS) return hipErrorNotSupported;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)corr_generic,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, GEN_LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     dim3 grid((a.Wo + GT - 1) / GT, (a.Ho + GT - 1) / GT);
-    hipLaunchKernelGGL(corr_generic, grid, dim3(256), lds, st, a, t, S, Q, pitch, rowsT);
+    hipLaunchKernelGGL(corr_generic, grid, dim3(256), lds, st, a, t, S, Q, pitch, rowsT, jb, kb);
     return hipGetLastError();
 }
 

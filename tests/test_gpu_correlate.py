@@ -67,6 +67,21 @@ def test_generic_shapes(oracle_mod, H, W, hT, wT, seed):
     _compare(oracle_mod, c["img"], c["tpl"], d)
 
 
+@pytest.mark.parametrize("H,W,hT,wT,seed", [
+    (40, 3000, 2, 2500, 31),   # wide: blocks of template dwords
+    (2300, 40, 2200, 3, 32),   # tall: blocks of template rows
+    (230, 420, 150, 200, 33),  # K = 30000, both
+    (2, 33100, 1, 33025, 34),  # K at its bound, one row
+    (33100, 3, 33025, 1, 35),  # K at its bound, one column
+])
+def test_large_templates_in_blocks(oracle_mod, H, W, hT, wT, seed):
+    """Templates whose tile + halo exceed the LDS: the blocked generic kernel."""
+    d = need_gpu()
+    announce("correlate large template %dx%d img %dx%d" % (hT, wT, H, W))
+    c = synth.random_case(seed, H, W, hT, wT, nTpl=1, kind="uniform")
+    _compare(oracle_mod, c["img"], c["tpl"], d)
+
+
 def test_medium_config(oracle_mod):
     """1024 x 1024 smooth noise, 32 x 32 template cut with +-8 noise."""
     d = need_gpu()
