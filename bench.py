@@ -302,10 +302,19 @@ def main():
         time_steps([sat2, boxes], 0, 3)
         t_b, t_q = time_each([sat2, boxes], 20, stream)
         rate = sat_bytes / (t_b * 1e-3) / 1e9
+        # the single-pass (look-back) build of the same tables, for comparison
+        os.environ["NCC_SAT_PATH"] = "fused"
+        try:
+            time_steps([sat2], 0, 3)
+            t_f, = time_each([sat2], 20, stream)
+        finally:
+            os.environ.pop("NCC_SAT_PATH", None)
         out["sat_workload"] = {
             "workload": "4096x4096 u8 uniform: ncc_sat_build, then 1,000,000 box queries on S and on Q",
             "sat_build_ms": round(t_b, 5), "sat_build_GB/s": round(rate, 1),
             "sat_build_frac_hbm": round(rate / HBM_PEAK_GBS, 4),
+            "single_pass_build_ms": round(t_f, 5),
+            "single_pass_build_GB/s": round(sat_bytes / (t_f * 1e-3) / 1e9, 1),
             "box_2x1M_ms": round(t_q, 5), "box_Mquery/s": round(2 * n / (t_q * 1e-3) / 1e6, 1)}
 
         wb = synth.make("bank")

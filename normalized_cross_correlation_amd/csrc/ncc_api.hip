@@ -60,6 +60,67 @@ int get_work(hipStream_t st, size_t bytes, void **out) {
     return NCC_OK;
 }
 
+// State of the single-pass table build for (current device, stream): kept
+// between calls and zero-filled when (re)allocated.  Same growth rules as
+// the workspace.
+std::map<std::pair<int, hipStream_t>, Work> g_state;
+
+int get_state(hipStream_t st, size_t bytes, void **out, size_t *have) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return NCC_EHIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    Work &w = g_state[std::make_pair(dev, st)];
+    if (w.bytes >= bytes && w.ptr) {
+        *out = w.ptr;
+        *have = w.bytes;
+        return NCC_OK;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return NCC_EHIP;
+    if (cs != hipStreamCaptureStatusNone) return NCC_EUNSUPPORTED;
+    if (w.ptr) {
+        if (hipStreamSynchronize(st) != hipSuccess) return NCC_EHIP;
+        if (hipFree(w.ptr) != hipSuccess) return NCC_EHIP;
+        w.ptr = nullptr;
+        w.bytes = 0;
+    }
+    if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        w.ptr = nullptr;
+        return NCC_ENOMEM;
+    }
+    if (hipMemsetAsync(w.ptr, 0, bytes, st) != hipSuccess) {
+        (void)hipFree(w.ptr);
+        w.ptr = nullptr;
+        return NCC_EHIP;
+    }
+    w.bytes = bytes;
+    *out = w.ptr;
+    *have = bytes;
+    return NCC_OK;
+}
+
+// Table build route: NCC_SAT_PATH = "fused" (single pass) or "passes".
+bool sat_fused_from_env() {
+    const char *e = std::getenv("NCC_SAT_PATH");
+    return e && !std::strcmp(e, "fused");
+}
+
+// Builds S and Q on `st`, with `wk` (three-pass scratch) carved by the caller.
+int build_tables(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q, const SatWork &wk,
+                 hipStream_t st) {
+    SatState fs{nullptr, nullptr, 0};
+    if (sat_fused_from_env()) {
+        void *p = nullptr;
+        size_t have = 0;
+        int rc = get_state(st, sat_state_bytes(W, H), &p, &have);
+        if (rc != NCC_OK) return rc;
+        fs = sat_state_view(p, have);
+    }
+    hipError_t e = sat_build_launch(img, W, H, S, Q, wk, fs, st);
+    return e == hipSuccess ? NCC_OK : (e == hipErrorNotSupported ? NCC_EUNSUPPORTED : NCC_EHIP);
+}
+
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int hip_status(hipError_t e) {
@@ -107,7 +168,7 @@ int ncc_sat_build(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q, void
     int rc = get_work(st, sat_work_bytes(W, H), &ws);
     if (rc != NCC_OK) return rc;
     SatWork wk = sat_work_carve(ws, W, H);
-    return hip_status(sat_build_launch(img, W, H, S, Q, wk, st));
+    return build_tables(img, W, H, S, Q, wk, st);
 }
 
 int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n, int64_t *out,
@@ -192,8 +253,8 @@ int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl, int wT, 
     if (need_tables) {
         int64_t *Sm = (int64_t *)(base + off_S), *Qm = (int64_t *)(base + off_Q);
         SatWork wk = sat_work_carve(base + off_sat, W, H);
-        e = sat_build_launch(img, W, H, Sm, Qm, wk, st);
-        if (e != hipSuccess) return hip_status(e);
+        rc = build_tables(img, W, H, Sm, Qm, wk, st);
+        if (rc != NCC_OK) return rc;
         S = Sm;
         Q = Qm;
     }
@@ -216,6 +277,14 @@ void ncc_release(void) {
         }
     }
     g_work.clear();
+    for (auto &kv : g_state) {
+        if (!kv.second.ptr) continue;
+        if (hipSetDevice(kv.first.first) == hipSuccess) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(kv.second.ptr);
+        }
+    }
+    g_state.clear();
     (void)hipSetDevice(cur);
 }
 

@@ -28,10 +28,29 @@ struct SatWork {
                         //   each downsweep tile row
 };
 
+// State of the single-pass build, kept per (device, stream) between calls:
+// ctl = {next tile ticket, finished tiles, call epoch, spin-limit flag} and
+// two parity buffers of published tile words ([2][capTiles][SAT_FWORDS]
+// uint64).  A call works in buffer epoch & 1 and clears the other one for
+// the next call; the last tile to finish resets the counters and advances
+// the epoch.  Zero-filled when allocated.
+struct SatState {
+    uint32_t *ctl;
+    uint64_t *words;
+    int capTiles;
+};
+constexpr int SAT_FW = 128;          // single-pass tile: columns
+constexpr int SAT_FSUB = 4;          // ... bands of SAT_BH rows
+constexpr int SAT_FWORDS = 4 * 128;  // words per tile: rows [2][128], columns [2][128]
+size_t sat_state_bytes(int W, int H);
+SatState sat_state_view(void *base, size_t bytes);
+
 size_t sat_work_bytes(int W, int H);
 SatWork sat_work_carve(void *base, int W, int H);
+// fs.ctl == nullptr: the three-pass build; else the single-pass build
 hipError_t sat_build_launch(const uint8_t *img, int W, int H, int64_t *S,
-                            int64_t *Q, const SatWork &wk, hipStream_t st);
+                            int64_t *Q, const SatWork &wk, const SatState &fs,
+                            hipStream_t st);
 
 hipError_t box_launch(const int64_t *S, int W, int H, const int32_t *rects,
                       int64_t n, int64_t *out, hipStream_t st);

@@ -432,6 +432,268 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
     }
 }
 
+
+// ----------------------------------------------------------- single pass --
+// One kernel: a workgroup takes a ticket (tiles in band-major order), loads
+// its 128 x 128 tile once, publishes its row sums and column sums, reads
+// what it needs of earlier tiles' published words, and writes its part of S
+// and Q.  Every published value is a 64-bit word value << 2 | state, stored
+// and read with single-copy-atomic relaxed accesses, so no fence orders data
+// against a flag.
+//   row word (tile, table, row):   1 = the tile's row sum, 2 = that plus the
+//                                  sum of the row left of the tile
+//   column word (tile, table, x):  1 = V(x) = sum over the tile's rows of the
+//                                  row running sum at x (from the image's
+//                                  left edge), 2 = the table value on the
+//                                  tile's last row
+// A tile waits only for words of tiles with smaller tickets, whose
+// workgroups are already running: the row words of state 1 are published
+// right after a tile's loads, the column words of state 1 after its row
+// look-back, which itself waits only for state-1 row words.  Each wait gives
+// up after SAT_FSPIN polls and raises ctl[3].
+constexpr int SAT_FSPIN = 1 << 22;
+constexpr int SAT_FBATCH = 8;
+
+__device__ __forceinline__ uint64_t word_load(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void word_store(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum of the values of the words at p - stride, p - 2*stride, ... (n of
+// them), stopping after the first one of state 2; waits for words of state 0.
+__device__ __forceinline__ uint64_t look_back(const uint64_t *p, size_t stride, int n,
+                                              uint32_t *ctl) {
+    uint64_t acc = 0;
+    for (int i0 = 0; i0 < n; i0 += SAT_FBATCH) {
+        uint64_t v[SAT_FBATCH];
+#pragma unroll
+        for (int k = 0; k < SAT_FBATCH; k++)
+            v[k] = i0 + k < n ? word_load(p - (size_t)(i0 + k + 1) * stride) : 2ull;
+        bool done = false;
+#pragma unroll
+        for (int k = 0; k < SAT_FBATCH; k++) {
+            if (!done) {
+                int spins = 0;
+                while ((v[k] & 3) == 0) {
+                    if (++spins > SAT_FSPIN) {
+                        __hip_atomic_store(ctl + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                    v[k] = word_load(p - (size_t)(i0 + k + 1) * stride);
+                }
+                acc += v[k] >> 2;
+                done = (v[k] & 3) == 2;
+            }
+        }
+        if (done) break;
+    }
+    return acc;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img, int W, int H,
+                                                 SatState fs, int nS, int nTiles,
+                                                 int64_t *__restrict__ S, int64_t *__restrict__ Q) {
+    constexpr int TR = SAT_BH * SAT_FSUB;  // tile rows
+    __shared__ int sh_tile;
+    __shared__ uint32_t sh_epoch;
+    __shared__ uint32_t colp[4][2][SAT_FW];  // per wavefront: pixel column sums of its rows
+    __shared__ uint32_t rtS[2][TR];          // row sums inside the tile
+    __shared__ uint32_t lrowS[2][TR];        // row sums left of the tile
+    __shared__ uint32_t csS[2][SAT_FW];      // running sums along the tile of the column sums
+    __shared__ uint64_t topS[2][SAT_FW];     // table values on the row above the tile
+    __shared__ uint64_t llS[4];              // per wavefront: sum of its lanes' left carries
+    __shared__ uint32_t wtS[4];              // per wavefront: column-sum scan totals
+    __shared__ uint64_t part[2][4][4][64];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    if (tid == 0) {
+        sh_tile = (int)__hip_atomic_fetch_add(fs.ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh_epoch = __hip_atomic_load(fs.ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const int tile = sh_tile;
+    const uint32_t epoch = sh_epoch;
+    if (tile >= nTiles) {  // counters not reset by the previous call: flag it, touch nothing
+        if (tid == 0) __hip_atomic_store(fs.ctl + 3, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const int gi = tile / nS, j = tile % nS;
+    uint64_t *words = fs.words + (size_t)(epoch & 1) * fs.capTiles * SAT_FWORDS;
+    {   // this workgroup's share of the next call's words
+        uint64_t *nxt = fs.words + (size_t)((epoch & 1) ^ 1) * fs.capTiles * SAT_FWORDS;
+        const size_t total = (size_t)fs.capTiles * SAT_FWORDS;
+        const size_t per = (total + nTiles - 1) / nTiles;
+        const size_t b = (size_t)tile * per, e = min(total, b + per);
+        for (size_t i = b + tid; i < e; i += 256) nxt[i] = 0;
+    }
+    uint64_t *my = words + (size_t)tile * SAT_FWORDS;
+
+    const int x = j * SAT_FW + 2 * l;
+    const int ytile = gi * TR;
+
+    // ---- the tile's own sums, band by band: row sums (published as soon as
+    // a band is done) and column sums of the pixels
+    const int tb = tid >> 7, ix = tid & 127;  // (table, row or column) of this thread's words
+    uint32_t c1a = 0, c1b = 0, c2a = 0, c2b = 0;
+#pragma unroll
+    for (int k = 0; k < SAT_FSUB; k++) {
+        uint32_t px[WAVE_ROWS];
+#pragma unroll
+        for (int r = 0; r < WAVE_ROWS; r++)
+            px[r] = load2<VEC>(img, W, H, x, ytile + SAT_BH * k + WAVE_ROWS * w + r);
+#pragma unroll
+        for (int r = 0; r < WAVE_ROWS; r++) {
+            const uint32_t b0 = px[r] & 0xffu, b1 = (px[r] >> 8) & 0xffu;
+            const uint32_t q0 = b0 * b0, q1 = b1 * b1;
+            const uint32_t t1 = wave_sum_u32(b0 + b1), t2 = wave_sum_u32(q0 + q1);
+            if (l == 0) {
+                rtS[0][SAT_BH * k + WAVE_ROWS * w + r] = t1;
+                rtS[1][SAT_BH * k + WAVE_ROWS * w + r] = t2;
+            }
+            c1a += b0;
+            c1b += b1;
+            c2a += q0;
+            c2b += q1;
+        }
+    }
+    *(uint2 *)&colp[w][0][2 * l] = make_uint2(c1a, c1b);
+    *(uint2 *)&colp[w][1][2 * l] = make_uint2(c2a, c2b);
+    __syncthreads();
+    {
+        word_store(my + tb * TR + ix, (uint64_t)rtS[tb][ix] << 2 | 1u);
+        const uint32_t cs = colp[0][tb][ix] + colp[1][tb][ix] + colp[2][tb][ix] + colp[3][tb][ix];
+        const uint32_t inc = wave_incl_scan_u32(cs);
+        if (l == 63) wtS[w] = inc;
+        __syncthreads();
+        csS[tb][ix] = inc + ((w & 1) ? wtS[w - 1] : 0u);
+    }
+
+    // ---- row look-back: the sum of each row left of the tile
+    {
+        const uint32_t rt = rtS[tb][ix];
+        const uint32_t lc = (uint32_t)look_back(my + tb * TR + ix, SAT_FWORDS, j, fs.ctl);
+        word_store(my + tb * TR + ix, (uint64_t)(lc + rt) << 2 | 2u);
+        lrowS[tb][ix] = lc;
+        const uint64_t s = wave_incl_scan_u64((uint64_t)lc);
+        if (l == 63) llS[w] = s;
+    }
+    __syncthreads();
+    // ---- column look-back: the table value above the tile
+    {
+        const uint64_t LL = llS[2 * tb] + llS[2 * tb + 1];
+        const uint64_t V = (uint64_t)csS[tb][ix] + LL;
+        uint64_t *cw = my + 2 * TR + tb * SAT_FW + ix;
+        word_store(cw, V << 2 | 1u);
+        const uint64_t C = look_back(cw, (size_t)nS * SAT_FWORDS, gi, fs.ctl);
+        word_store(cw, (C + V) << 2 | 2u);
+        topS[tb][ix] = C;
+    }
+    __syncthreads();
+
+    // ---- the tile's rows of S and Q, band by band (as the downsweep; the
+    // bytes are read again, mostly from L2, the next band's in flight while
+    // the current one is stored)
+    uint64_t s1a = topS[0][2 * l], s1b = topS[0][2 * l + 1];
+    uint64_t s2a = topS[1][2 * l], s2b = topS[1][2 * l + 1];
+    typedef long long v2l __attribute__((ext_vector_type(2)));
+    const bool pair = VEC && x + 1 < W;
+    uint32_t pc[WAVE_ROWS], pn[WAVE_ROWS];
+#pragma unroll
+    for (int r = 0; r < WAVE_ROWS; r++) pc[r] = load2<VEC>(img, W, H, x, ytile + WAVE_ROWS * w + r);
+#pragma unroll
+    for (int k = 0; k < SAT_FSUB; k++) {
+        const int yb = ytile + SAT_BH * k;
+        if (yb >= H) break;  // workgroup-uniform
+        const int y0 = yb + WAVE_ROWS * w;
+        const int rr = SAT_BH * k + WAVE_ROWS * w + (l & (WAVE_ROWS - 1));
+        const uint32_t lc1 = lrowS[0][rr], lc2 = lrowS[1][rr];
+        uint32_t R1a[WAVE_ROWS], R1b[WAVE_ROWS], R2a[WAVE_ROWS], R2b[WAVE_ROWS];
+        uint64_t d1a = 0, d1b = 0, d2a = 0, d2b = 0;
+#pragma unroll
+        for (int r = 0; r < WAVE_ROWS; r++) {
+            const uint32_t b0 = pc[r] & 0xffu, b1 = (pc[r] >> 8) & 0xffu;
+            const uint32_t p1 = b0 + b1, p2 = b0 * b0 + b1 * b1;
+            const uint32_t e1 = wave_incl_scan_u32(p1) - p1 +
+                                (uint32_t)__builtin_amdgcn_readlane((int)lc1, r);
+            const uint32_t e2 = wave_incl_scan_u32(p2) - p2 +
+                                (uint32_t)__builtin_amdgcn_readlane((int)lc2, r);
+            R1a[r] = e1 + b0;
+            R1b[r] = e1 + p1;
+            R2a[r] = e2 + b0 * b0;
+            R2b[r] = e2 + p2;
+            d1a += R1a[r];
+            d1b += R1b[r];
+            d2a += R2a[r];
+            d2b += R2b[r];
+        }
+        if (k + 1 < SAT_FSUB) {
+#pragma unroll
+            for (int r = 0; r < WAVE_ROWS; r++) pn[r] = load2<VEC>(img, W, H, x, y0 + SAT_BH + r);
+        }
+        const int pb = k & 1;
+        part[pb][w][0][l] = d1a;
+        part[pb][w][1][l] = d1b;
+        part[pb][w][2][l] = d2a;
+        part[pb][w][3][l] = d2b;
+        __syncthreads();
+        uint64_t t1a = s1a, t1b = s1b, t2a = s2a, t2b = s2b;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) {
+            const uint64_t u1a = part[pb][ww][0][l], u1b = part[pb][ww][1][l];
+            const uint64_t u2a = part[pb][ww][2][l], u2b = part[pb][ww][3][l];
+            if (ww < w) {
+                t1a += u1a;
+                t1b += u1b;
+                t2a += u2a;
+                t2b += u2b;
+            }
+            s1a += u1a;
+            s1b += u1b;
+            s2a += u2a;
+            s2b += u2b;
+        }
+#pragma unroll
+        for (int r = 0; r < WAVE_ROWS; r++) {
+            const int y = y0 + r;
+            if (y >= H) break;
+            t1a += R1a[r];
+            t1b += R1b[r];
+            t2a += R2a[r];
+            t2b += R2b[r];
+            int64_t *srow = S + (size_t)y * W + x;
+            int64_t *qrow = Q + (size_t)y * W + x;
+            if (pair) {
+                *(v2l *)srow = v2l{(long long)t1a, (long long)t1b};
+                *(v2l *)qrow = v2l{(long long)t2a, (long long)t2b};
+            } else {
+                if (x < W) {
+                    srow[0] = (int64_t)t1a;
+                    qrow[0] = (int64_t)t2a;
+                }
+                if (x + 1 < W) {
+                    srow[1] = (int64_t)t1b;
+                    qrow[1] = (int64_t)t2b;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < WAVE_ROWS; r++) pc[r] = pn[r];
+    }
+
+    // ---- the last tile to finish resets the counters for the next call
+    if (tid == 0) {
+        const uint32_t d = __hip_atomic_fetch_add(fs.ctl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == (uint32_t)nTiles - 1) {
+            __hip_atomic_store(fs.ctl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(fs.ctl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(fs.ctl + 2, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 }  // namespace
 
 size_t sat_work_bytes(int W, int H) {
@@ -463,8 +725,37 @@ SatWork sat_work_carve(void *base, int W, int H) {
     return wk;
 }
 
+size_t sat_state_bytes(int W, int H) {
+    const size_t nS = (W + SAT_FW - 1) / SAT_FW;
+    const size_t nG = (H + SAT_BH * SAT_FSUB - 1) / (SAT_BH * SAT_FSUB);
+    return 256 + 2 * nS * nG * SAT_FWORDS * sizeof(uint64_t);
+}
+
+SatState sat_state_view(void *base, size_t bytes) {
+    SatState fs;
+    fs.ctl = (uint32_t *)base;
+    fs.words = (uint64_t *)((char *)base + 256);
+    fs.capTiles = (int)((bytes - 256) / (2 * SAT_FWORDS * sizeof(uint64_t)));
+    return fs;
+}
+
 hipError_t sat_build_launch(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q,
-                            const SatWork &wk, hipStream_t st) {
+                            const SatWork &wk, const SatState &fs, hipStream_t st) {
+    if (fs.ctl) {
+        const int nS = (W + SAT_FW - 1) / SAT_FW;
+        const int nG = (H + SAT_BH * SAT_FSUB - 1) / (SAT_BH * SAT_FSUB);
+        const int nTiles = nS * nG;
+        if (nTiles > fs.capTiles) return hipErrorInvalidValue;
+        const bool vec = (W % 2 == 0) && (((uintptr_t)img & 1) == 0) &&
+                         (((uintptr_t)S & 15) == 0) && (((uintptr_t)Q & 15) == 0);
+        if (vec)
+            hipLaunchKernelGGL(sat_fused<true>, dim3(nTiles), dim3(256), 0, st, img, W, H, fs, nS,
+                               nTiles, S, Q);
+        else
+            hipLaunchKernelGGL(sat_fused<false>, dim3(nTiles), dim3(256), 0, st, img, W, H, fs, nS,
+                               nTiles, S, Q);
+        return hipGetLastError();
+    }
     // aligned 16-byte image rows (and band rows) for the row pass; even
     // widths and 16-byte table rows for the paired loads and stores of the
     // downsweep

@@ -1,7 +1,11 @@
 """GPU parity of the summed-area table build and box queries against the oracle.
 
-Tables and box sums are integers: they must match bit for bit.
+Tables and box sums are integers: they must match bit for bit.  Every test
+runs on both builds of the library: the three-pass build (default) and the
+single-pass look-back build (NCC_SAT_PATH=fused).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -9,6 +13,17 @@ from normalized_cross_correlation_amd import synth
 from tests.gpu_util import announce, dev, host, need_gpu
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, params=["passes", "fused"])
+def sat_route(request):
+    old = os.environ.get("NCC_SAT_PATH")
+    os.environ["NCC_SAT_PATH"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("NCC_SAT_PATH", None)
+    else:
+        os.environ["NCC_SAT_PATH"] = old
 
 SHAPES = [
     # H, W: single pixel, thin, below one tile, ragged tails in both directions,
@@ -22,7 +37,7 @@ SHAPES = [
 def test_sat_matches_oracle(oracle_mod, H, W):
     import normalized_cross_correlation_amd as ncc
     d = need_gpu()
-    announce("sat %dx%d" % (H, W))
+    announce("sat %dx%d route=%s" % (H, W, os.environ.get("NCC_SAT_PATH")))
     rng = np.random.default_rng(H * 10007 + W)
     img = rng.integers(0, 256, (H, W), dtype=np.uint8)
     S, Q = ncc.sat_build(dev(img, d))

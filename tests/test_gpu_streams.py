@@ -24,14 +24,18 @@ def _eager(ncc, img, tpl):
     return host(S), host(Q), host(coef), host(sums)
 
 
-@pytest.mark.parametrize("tshape", [(16, 16, 1), (16, 16, 20), (9, 11, 1)])
-def test_graph_capture_replays(tshape):
-    """Table build + correlation captured once, replayed on changing images."""
+@pytest.mark.parametrize("tshape,sat_path", [((16, 16, 1), "passes"), ((16, 16, 20), "passes"),
+                                             ((9, 11, 1), "passes"), ((16, 16, 1), "fused")])
+def test_graph_capture_replays(tshape, sat_path, monkeypatch):
+    """Table build + correlation captured once, replayed on changing images.
+    The single-pass table build keeps its call counters on the device, so its
+    replays need nothing from the host either."""
     import torch
     import normalized_cross_correlation_amd as ncc
     d = need_gpu()
+    monkeypatch.setenv("NCC_SAT_PATH", sat_path)
     hT, wT, n = tshape
-    announce("graph capture tpl %dx%d n=%d" % (hT, wT, n))
+    announce("graph capture tpl %dx%d n=%d sat=%s" % (hT, wT, n, sat_path))
     cases = [synth.random_case(60 + i, 173, 301, hT, wT, nTpl=n, kind="smooth") for i in range(3)]
     img = dev(cases[0]["img"], d)
     tpl = dev(cases[0]["tpl"], d)
@@ -93,11 +97,14 @@ def test_two_streams_concurrent():
         np.testing.assert_array_equal(host(sb), ref_b[3])
 
 
-def test_workspace_regrowth_between_calls():
-    """Sizes that grow and shrink on one stream reuse or regrow its workspace."""
+@pytest.mark.parametrize("sat_path", ["passes", "fused"])
+def test_workspace_regrowth_between_calls(sat_path, monkeypatch):
+    """Sizes that grow and shrink on one stream reuse or regrow its workspace
+    (and, for the single-pass table build, its call state)."""
     import normalized_cross_correlation_amd as ncc
     d = need_gpu()
-    announce("workspace regrowth")
+    monkeypatch.setenv("NCC_SAT_PATH", sat_path)
+    announce("workspace regrowth sat=%s" % sat_path)
     refs = []
     shapes = [(40, 70, 16, 16, 3), (400, 900, 16, 16, 1), (33, 50, 5, 7, 2), (500, 1000, 16, 16, 64),
               (20, 20, 4, 4, 1)]
