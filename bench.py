@@ -343,6 +343,52 @@ def main():
             assert abs(float(bcoef[t, y, x]) - 1.0) <= 1e-5
         del bcoef
 
+        # the same bank through the rectangle entry point with every position
+        # and output rows padded to 4096 floats: each row starts 256-byte
+        # aligned, which the dense 4081-float rows do not
+        op = (Wo + 63) // 64 * 64
+        pcoef = torch.empty((nb, Ho, op), dtype=torch.float32, device=d)
+        ppc = pcoef.data_ptr()
+
+        def bank_pitched():
+            assert L.ncc_correlate_rect(pbi, W, H, W, pbt, wT, hT, nb, 0, 0, Wo, Ho, op, None,
+                                        ppc, sh) == 0
+
+        time_steps([bank_pitched], 0, 2)
+        t_kp, = time_each([bank_pitched], 10, stream)
+        for (x, y), t in zip(wb["cut_xy"], range(nb)):
+            assert abs(float(pcoef[t, y, x]) - 1.0) <= 1e-5
+        del pcoef
+        bwp = out_bytes / (t_kp * 1e-3) / 1e9
+        out["bank_workload"].update({
+            "pitched_output_ms": round(t_kp, 4),
+            "pitched_output_Gcoeff/s": round(bcoeffs / (t_kp * 1e-3) / 1e9, 1),
+            "pitched_output_hbm_GB/s": round(bwp, 1),
+            "pitched_output": "ncc_correlate_rect over every position, out_pitch %d floats" % op})
+
+        # search rectangles on the headline image (ncc_correlate_rect, in
+        # place, dense output): a local search around the template's origin
+        # and a large sub-image, both at offsets that are not 16-byte aligned
+        (cx, cy), = w["cut_xy"]
+        rect_out = {"workload": "4096x4096 headline image, 16x16 template: ncc_correlate_rect"}
+        for name, (rw, rh) in (("local_256", (256, 256)), ("sub_2048", (2048, 2048))):
+            x0 = min(max(cx - rw // 2, 0), Wo - rw) | 1
+            y0 = min(max(cy - rh // 2, 0), Ho - rh) | 1
+            x0, y0 = min(x0, Wo - rw), min(y0, Ho - rh)
+            rcoef = torch.empty((1, rh, rw), dtype=torch.float32, device=d)
+            prc = rcoef.data_ptr()
+
+            def rect(x0=x0, y0=y0, rw=rw, rh=rh, prc=prc):
+                assert L.ncc_correlate_rect(pi, W, H, W, pt, wT, hT, 1, x0, y0, rw, rh, rw, None,
+                                            prc, sh) == 0
+
+            time_steps([rect], 0, 3)
+            t_r, = time_each([rect], 20, stream)
+            assert abs(float(rcoef[0, cy - y0, cx - x0]) - 1.0) <= 1e-5
+            rect_out[name] = {"origin": [x0, y0], "size": [rw, rh], "us": round(t_r * 1e3, 2),
+                              "Gcoeff/s": round(rw * rh / (t_r * 1e-3) / 1e9, 1)}
+        out["rect_workload"] = rect_out
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(img_np, tpl_np[0])
     print(json.dumps(out), flush=True)

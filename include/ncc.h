@@ -15,7 +15,8 @@
  *     query with the table's two leading edges read as zero.
  *
  * Conventions for every entry point:
- *   - Images are H rows x W columns of uint8, row-major, dense (pitch = W).
+ *   - Images are H rows x W columns of uint8, row-major, dense (pitch = W),
+ *     except where an entry point takes a pitch.
  *   - Buffer arguments are DEVICE pointers (memory from hipMalloc or from a
  *     framework allocator on the current device).  The caller allocates and
  *     owns them; the library never frees or keeps them.
@@ -31,6 +32,7 @@
 #ifndef NCC_H
 #define NCC_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -125,6 +127,54 @@ int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n,
 int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl,
                   int wT, int hT, int nTpl, int32_t *sums_out,
                   float *coef_out, void *stream);
+
+/* Largest output row pitch of ncc_correlate_rect, in elements. */
+#define NCC_MAX_OUT_PITCH (1 << 24)
+
+/*
+ * ncc_correlate_rect -- the same correlation over a rectangle of positions
+ * only, read in place from a pitched image, written to pitched output
+ * ("Image in shared memory": the sample program's corrShared_kernel computes
+ * a w x h rectangle of coefficients whose upper-left position is offset into
+ * the image, into rows CorrPitch apart; the two offsets the listing adds to
+ * every image coordinate enter here as their sum, x0 and y0).
+ *
+ *   img        H rows of W uint8 pixels, device; row y starts at
+ *              img + y*img_pitch (img_pitch >= W bytes).
+ *   tpl        [nTpl][hT][wT] uint8, device.
+ *   x0, y0     the first position: its window covers rows y0..y0+hT-1 and
+ *              columns x0..x0+wT-1.
+ *   w, h       positions x0..x0+w-1 by y0..y0+h-1; every window must lie
+ *              inside the image: 0 <= x0, x0+w <= W-wT+1, 0 <= y0,
+ *              y0+h <= H-hT+1 (valid mode, as ncc_correlate).  w == 0 or
+ *              h == 0 writes nothing and returns NCC_OK.
+ *   out_pitch  elements from one output row to the next (>= w); planes are
+ *              h*out_pitch elements apart.  Elements between w and
+ *              out_pitch of each row are not written.
+ *   sums_out   nullable; [(2+nTpl)][h][out_pitch] int32, device, planes as in
+ *              ncc_correlate: element [p][v][u] belongs to position
+ *              (x0+u, y0+v).
+ *   coef_out   [nTpl][h][out_pitch] float32, device, likewise (may be NULL
+ *              when w or h is 0).
+ *
+ * Every value equals ncc_correlate's at the same position, bit for bit for
+ * the sums.  Only the image rows and columns that the rectangle's windows
+ * cover are read (the streaming kernel may also read up to 15 bytes on each
+ * side of them within the same image row).
+ *
+ * Errors: NCC_EINVAL (null img/tpl, null coef_out with w, h > 0, W or H < 1,
+ * wT or hT < 1, wT > W, hT > H, nTpl < 1, img_pitch < W, w or h < 0,
+ * out_pitch < w),
+ * NCC_ERANGE (the rectangle outside the valid positions,
+ * wT*hT > NCC_MAX_TEMPLATE_PIXELS, w+wT-1 > NCC_MAX_WIDTH,
+ * (w+wT-1)*(h+hT-1) > 2^40, img_pitch*H > 2^48,
+ * out_pitch > NCC_MAX_OUT_PITCH, outputs past 2^62 bytes), and the rest as
+ * ncc_correlate.
+ */
+int ncc_correlate_rect(const uint8_t *img, int W, int H, size_t img_pitch,
+                       const uint8_t *tpl, int wT, int hT, int nTpl,
+                       int x0, int y0, int w, int h, size_t out_pitch,
+                       int32_t *sums_out, float *coef_out, void *stream);
 
 /* Static string naming a status code. */
 const char *ncc_strerror(int status);

@@ -12,20 +12,24 @@ the tensor device's current torch stream:
 * ``sat_build(img)``             -> (S, Q) int64 summed-area tables
 * ``box(S, rects)``              -> int64 four-corner box sums
 * ``correlate(img, tpl, sums)``  -> (coef float32 [n][Ho][Wo], sums int32 or None)
+* ``correlate_rect(img, tpl, x0, y0, w, h)`` -> the same over a w x h rectangle
+  of positions, read in place from a row-strided image, written to row-strided
+  output
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["sat_build", "box", "correlate", "release", "lib", "NCCError",
+__all__ = ["sat_build", "box", "correlate", "correlate_rect", "release", "lib", "NCCError",
            "ABI_FUNCTIONS", "LIB_PATH", "MAX_WIDTH", "MAX_TEMPLATE_PIXELS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libncc.so")
-ABI_FUNCTIONS = ("ncc_sat_build", "ncc_box", "ncc_correlate", "ncc_strerror",
-                 "ncc_release", "ncc_version")
+ABI_FUNCTIONS = ("ncc_sat_build", "ncc_box", "ncc_correlate", "ncc_correlate_rect",
+                 "ncc_strerror", "ncc_release", "ncc_version")
 MAX_WIDTH = 66051
 MAX_TEMPLATE_PIXELS = 33025
+MAX_OUT_PITCH = 1 << 24
 
 _lib = None
 
@@ -52,6 +56,9 @@ def lib():
         L.ncc_box.restype = I
         L.ncc_correlate.argtypes = [P, I, I, P, I, I, I, P, P, P]
         L.ncc_correlate.restype = I
+        Z = ctypes.c_size_t
+        L.ncc_correlate_rect.argtypes = [P, I, I, Z, P, I, I, I, I, I, I, I, Z, P, P, P]
+        L.ncc_correlate_rect.restype = I
         L.ncc_strerror.argtypes = [I]
         L.ncc_strerror.restype = ctypes.c_char_p
         L.ncc_release.argtypes = []
@@ -158,6 +165,73 @@ def correlate(img, tpl, want_sums: bool = False, coef=None, sums=None):
         _check("ncc_correlate", lib().ncc_correlate(
             img.data_ptr(), W, H, tpl.data_ptr(), wT, hT, n,
             sums.data_ptr() if sums is not None else None, coef.data_ptr(), _stream(img)))
+    return coef, sums
+
+
+def _row_strided(t, dtype, name, ndim):
+    """A tensor whose last dimension is dense (rows may be strided)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a ROCm device" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions" % (name, ndim))
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("%s must have unit stride along its rows" % name)
+    return t
+
+
+def _pitched(t, name, planes, h, w):
+    """Row pitch (elements) of a [planes][h][w] output view whose planes are
+    h rows apart; None when the view does not fix it (one row in all)."""
+    if tuple(t.shape) != (planes, h, w):
+        raise ValueError("%s must be [%d][%d][%d]" % (name, planes, h, w))
+    if t.numel() == 0 or (h == 1 and planes == 1):
+        return None
+    pitch = t.stride(1) if h > 1 else t.stride(0)  # h == 1: one row per plane
+    if pitch < w or (planes > 1 and t.stride(0) != h * pitch):
+        raise ValueError("%s: planes must be h rows apart, rows >= w elements apart" % name)
+    return pitch
+
+
+def correlate_rect(img, tpl, x0: int, y0: int, w: int, h: int, want_sums: bool = False,
+                   out_pitch=None, coef=None, sums=None):
+    """NCC at the positions x0..x0+w-1 by y0..y0+h-1 only (each window inside
+    the image).  img is [H][W] uint8 with dense rows (a row-strided view, e.g.
+    a crop, is read in place).  Returns (coef float32 [n][h][w], sums int32
+    [2+n][h][w] or None), views of buffers whose rows are out_pitch (default
+    w) elements apart; coef / sums may be given as such views."""
+    import torch
+    _row_strided(img, torch.uint8, "img", 2)
+    if tpl.dim() == 2:
+        tpl = tpl.unsqueeze(0)
+    _dev_tensor(tpl, torch.uint8, "tpl", 3)
+    H, W = img.shape
+    ip = img.stride(0) if H > 1 else W
+    n, hT, wT = tpl.shape
+    given = [out_pitch] if out_pitch is not None else []
+    if coef is not None:
+        _row_strided(coef, torch.float32, "coef", 3)
+        given.append(_pitched(coef, "coef", n, h, w))
+    if sums is not None:
+        _row_strided(sums, torch.int32, "sums", 3)
+        given.append(_pitched(sums, "sums", 2 + n, h, w))
+    given = [p for p in given if p is not None]
+    if any(p != given[0] for p in given):
+        raise ValueError("out_pitch, coef and sums disagree on the output row pitch")
+    out_pitch = given[0] if given else w
+    if coef is None:
+        coef = torch.empty((n, h, out_pitch), dtype=torch.float32, device=img.device)[:, :, :w]
+    if want_sums and sums is None:
+        sums = torch.empty((2 + n, h, out_pitch), dtype=torch.int32, device=img.device)[:, :, :w]
+    with torch.cuda.device(img.device):
+        _check("ncc_correlate_rect", lib().ncc_correlate_rect(
+            img.data_ptr(), W, H, ip, tpl.data_ptr(), wT, hT, n, x0, y0, w, h, out_pitch,
+            sums.data_ptr() if sums is not None and sums.numel() else None,
+            coef.data_ptr() if coef.numel() else None, _stream(img)))
     return coef, sums
 
 

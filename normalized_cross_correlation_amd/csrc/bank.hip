@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
         const int y = y0 + r, xb = x0 + 4 * c;
         uint32_t v = 0;
         if (y < a.H) {
-            const uint8_t *row = a.img + (size_t)y * a.W;
+            const uint8_t *row = a.img + (size_t)y * a.ip;
             if (xb + 3 < a.W && ((((uintptr_t)row + xb) & 3) == 0)) {
                 v = *(const uint32_t *)(row + xb);
             } else {
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
             if (a.sums && bz == 0 && g0 == 0) {
                 const int y = y0 + 4 * rq + o, x = x0 + c;
                 if (y < a.Ho && x < a.Wo) {
-                    const size_t plane = (size_t)a.Ho * a.Wo, oo = (size_t)y * a.Wo + x;
+                    const size_t plane = a.oplane, oo = (size_t)y * a.op + x;
                     __builtin_nontemporal_store(sumI, a.sums + oo);
                     __builtin_nontemporal_store(sumISq, a.sums + plane + oo);
                 }
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
     // MFMA results into coefficients, transposes them through its LDS buffer
     // and writes 256 contiguous bytes per template row.
     float *ob = &obuf[w][0][0];
-    const size_t plane = (size_t)a.Ho * a.Wo;
+    const size_t plane = a.oplane;
     const bool whole = x0 + BX <= a.Wo;  // every column of the tile is an output
     for (int yy = w; yy < BY; yy += 4) {
         const int y = y0 + yy;
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
             sI4[mg] = *(const int4 *)&sIs[yy][16 * mg + 4 * g];
             rI4[mg] = *(const float4 *)&rIs[yy][16 * mg + 4 * g];
         }
-        const size_t orow = (size_t)y * a.Wo + x0;
+        const size_t orow = (size_t)y * a.op + x0;
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
             v4i acc[4];
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
                     const int xb = x0 + 16 * mg + 4 * g;
                     if (FULLT || tt < a.nTpl) {
                         const int sT = 128 * K - ca[nb];
-                        int32_t *sd = a.sums + (size_t)(2 + tt) * plane + (size_t)y * a.Wo + xb;
+                        int32_t *sd = a.sums + (size_t)(2 + tt) * plane + (size_t)y * a.op + xb;
 #pragma unroll
                         for (int i = 0; i < 4; i++)
                             if (xb + i < a.Wo)

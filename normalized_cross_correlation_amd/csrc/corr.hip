@@ -29,17 +29,21 @@
 // taken in blocks of rows x dwords, each block staging its part of the image.
 #include "ncc_internal.h"
 
+#include <cstdlib>
+
 namespace ncc {
 
 namespace {
 
 // ------------------------------------------------------ staging helpers --
-// Loads bytes [x, x+16) of row y as 4 dwords; bytes outside the image are 0.
+// Loads bytes [x, x+16) of row y (at img + y * ip) as 4 dwords; bytes
+// outside the image are 0.  ALIGN: the alignment of img and ip (and of x,
+// a multiple of 16).
 template <int ALIGN>
-__device__ __forceinline__ uint4 load16(const uint8_t *img, int W, int H, int x, int y) {
+__device__ __forceinline__ uint4 load16(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
     uint4 v = make_uint4(0, 0, 0, 0);
     if (y >= H || x >= W) return v;
-    const uint8_t *row = img + (size_t)y * W;
+    const uint8_t *row = img + (size_t)y * ip;
     if (ALIGN == 16 && x + 15 < W) return *(const uint4 *)(row + x);
     if (ALIGN >= 4 && x + 15 < W) {
         const uint32_t *p = (const uint32_t *)(row + x);
@@ -119,7 +123,7 @@ __device__ __forceinline__ float stream_coef(const StreamState<WT4, HT, POS> &st
 // the strip's last HT-1 output rows still end here); PHASE 1: all.
 template <int WT4, int HT, int POS, int Q, int PHASE>
 __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
-                                           const uint32_t (&d)[WT4 + 1], int rowsOut, int Wo) {
+                                           const uint32_t (&d)[WT4 + 1], int rowsOut, uint32_t op) {
     uint32_t v[POS][WT4];
 #pragma unroll
     for (int p = 0; p < POS; p++)
@@ -207,7 +211,7 @@ __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
         }
     }
     st.yrel++;
-    st.off += Wo;
+    st.off += op;
 }
 
 // Rows Q .. HT-1 of a batch; the LDS reads of row Q+1 are issued before row
@@ -215,17 +219,17 @@ __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
 template <int WT4, int HT, int POS, int Q, int PHASE>
 __device__ __forceinline__ void stream_rows(StreamState<WT4, HT, POS> &st, const uint32_t *rowbase,
                                             int pitch, uint32_t (&d)[WT4 + 1], int rowsOut,
-                                            int Wo) {
+                                            uint32_t op) {
     uint32_t dn[WT4 + 1];
     if constexpr (Q + 1 < HT) {
 #pragma unroll
         for (int k = 0; k <= WT4; k++) dn[k] = rowbase[(Q + 1) * pitch + k];
     }
-    stream_row<WT4, HT, POS, Q, PHASE>(st, d, rowsOut, Wo);
+    stream_row<WT4, HT, POS, Q, PHASE>(st, d, rowsOut, op);
     if constexpr (Q + 1 < HT) {
 #pragma unroll
         for (int k = 0; k <= WT4; k++) d[k] = dn[k];
-        stream_rows<WT4, HT, POS, Q + 1, PHASE>(st, rowbase, pitch, d, rowsOut, Wo);
+        stream_rows<WT4, HT, POS, Q + 1, PHASE>(st, rowbase, pitch, d, rowsOut, op);
     }
 }
 
@@ -253,13 +257,14 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
 
     StreamState<WT4, HT, POS> st;
     // the lane's columns; lanes past the last output column compute (and
-    // store) that column again
+    // store) that column again, lanes before the first one (xs) the first
     const int xf = x0 + POS * tid;
-    const int xa = min(xf, a.Wo - 1);
+    const int xa = max(min(xf, a.Wo - 1), a.xs);
     const int lxa = xa - x0;   // byte offset of the first window in a staged row
 #pragma unroll
-    for (int p = 0; p < POS; p++) st.sh[p] = (uint32_t)(min(xf + p, a.Wo - 1) - x0 - (lxa & ~3));
-    st.pairs = x0 + NC <= a.Wo;
+    for (int p = 0; p < POS; p++)
+        st.sh[p] = (uint32_t)(max(min(xf + p, a.Wo - 1), a.xs) - x0 - (lxa & ~3));
+    st.pairs = x0 >= a.xs && x0 + NC <= a.Wo;
 
     const int wT = a.wT;
     st.mlast = byte_mask(wT - 4 * (WT4 - 1));
@@ -298,10 +303,10 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
         for (int i = 0; i < HT; i++) st.acc[p][i] = st.pI[p][i] = st.pQ[p][i] = 0;
     }
     st.yrel = 0;
-    const size_t plane = (size_t)a.Ho * a.Wo;
+    const size_t plane = a.oplane;
     // per-strip bases keep the per-lane offset within 32 bits
-    const size_t o0 = (size_t)y0 * a.Wo;
-    st.off = (uint32_t)xa;
+    const size_t o0 = (size_t)y0 * a.op;
+    st.off = (uint32_t)(xa - a.xs);
     st.out = a.coef + (size_t)t * plane + o0;
     st.wsum = a.sums != nullptr;
     st.wfirst = t == 0;
@@ -318,15 +323,15 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
     const bool colsIn = ALIGN == 16 && x0 + 16 * CH <= a.W;
     auto fetch = [&](int bt) {
         if (ALIGN == 16) {
-            // W % 16 == 0: a chunk lies wholly inside or wholly outside the
-            // image; load from a clamped in-bounds address and zero what lies
-            // outside (a select, not a branch)
+            // W, ip % 16 == 0: a chunk lies wholly inside or wholly outside
+            // the image; load from a clamped in-bounds address and zero what
+            // lies outside (a select, not a branch)
 #pragma unroll
             for (int u = 0; u < LOADS; u++) {
                 const int i = tid + u * NT;
                 const int r = i / CH, c = i % CH;
                 const int y = y0 + bt * HT + r, x = x0 + 16 * c;
-                const uint4 v = *(const uint4 *)(a.img + (size_t)min(y, a.H - 1) * a.W + min(x, a.W - 16));
+                const uint4 v = *(const uint4 *)(a.img + (size_t)min(y, a.H - 1) * a.ip + min(x, a.W - 16));
                 const bool ok = i < HT * CH && y < a.H && x < a.W;
                 pre[u] = ok ? v : make_uint4(0, 0, 0, 0);
             }
@@ -339,7 +344,7 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
                 const int i = tid + u * NT;
                 const int r = i / CH, c = i % CH;
                 pre[u] = (i < HT * CH)
-                             ? *(const uint4 *)(a.img + (size_t)(y0 + bt * HT + r) * a.W + x0 + 16 * c)
+                             ? *(const uint4 *)(a.img + (size_t)(y0 + bt * HT + r) * a.ip + x0 + 16 * c)
                              : make_uint4(0, 0, 0, 0);
             }
         } else {
@@ -348,7 +353,7 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
                 const int i = tid + u * NT;
                 const int r = i / CH, c = i % CH;
                 pre[u] = (i < HT * CH)
-                             ? load16<ALIGN>(a.img, a.W, a.H, x0 + 16 * c, y0 + bt * HT + r)
+                             ? load16<ALIGN>(a.img, a.ip, a.W, a.H, x0 + 16 * c, y0 + bt * HT + r)
                              : make_uint4(0, 0, 0, 0);
             }
         }
@@ -380,7 +385,7 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
     if (nb > 1) fetch(1);
 #pragma unroll
     for (int k = 0; k <= WT4; k++) d[k] = rowbase0[k];
-    stream_rows<WT4, HT, POS, 0, 0>(st, rowbase0, PITCH, d, rowsOut, a.Wo);
+    stream_rows<WT4, HT, POS, 0, 0>(st, rowbase0, PITCH, d, rowsOut, (uint32_t)a.op);
     if (nb > 1) put(1);
     __syncthreads();
     // full batches
@@ -389,7 +394,7 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
         const uint32_t *rowbase = rowbase0 + (bt & 1) * HT * PITCH;
 #pragma unroll
         for (int k = 0; k <= WT4; k++) d[k] = rowbase[k];
-        stream_rows<WT4, HT, POS, 0, 1>(st, rowbase, PITCH, d, rowsOut, a.Wo);
+        stream_rows<WT4, HT, POS, 0, 1>(st, rowbase, PITCH, d, rowsOut, (uint32_t)a.op);
         if (bt + 1 < nb) put(bt + 1);
         __syncthreads();
     }
@@ -398,7 +403,7 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
         const uint32_t *rowbase = rowbase0 + ((nb - 1) & 1) * HT * PITCH;
 #pragma unroll
         for (int k = 0; k <= WT4; k++) d[k] = rowbase[k];
-        stream_rows<WT4, HT, POS, 0, 2>(st, rowbase, PITCH, d, rowsOut, a.Wo);
+        stream_rows<WT4, HT, POS, 0, 2>(st, rowbase, PITCH, d, rowsOut, (uint32_t)a.op);
     }
 }
 
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int
                 const int y = y0 + j0 + r, xb = x0 + 4 * (k0 + c);
                 uint32_t v = 0;
                 if (y < a.H) {
-                    const uint8_t *row = a.img + (size_t)y * a.W;
+                    const uint8_t *row = a.img + (size_t)y * a.ip;
 #pragma unroll
                     for (int bb = 0; bb < 4; bb++)
                         if (xb + bb < a.W) v |= (uint32_t)row[xb + bb] << (8 * bb);
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int
 
     const TStat ts = a.stats[t];
     const long long K = (long long)a.wT * a.hT;
-    const size_t plane = (size_t)a.Ho * a.Wo;
+    const size_t plane = a.oplane;
 #pragma unroll
     for (int dy = 0; dy < 4; dy++) {
         const int y = y0 + 4 * ty + dy;
@@ -500,7 +505,7 @@ __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int
             const long long num = K * sumIT - sumI * ts.sumT;
             const long long varI = K * sumISq - sumI * sumI;
             const float g = ncc_coef((float)num, (float)varI, ts.varTf);
-            const size_t o = (size_t)y * a.Wo + x;
+            const size_t o = (size_t)y * a.op + x;
             store_coef(a.coef + (size_t)t * plane + o, g);
             if (a.sums) {
                 if (t == 0) {
@@ -516,31 +521,78 @@ __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int
 #ifndef NCC_STREAM_WAVES
 #define NCC_STREAM_WAVES 4
 #endif
-#ifndef NCC_STREAM_RS
-#define NCC_STREAM_RS 64
-#endif
 #ifndef NCC_STREAM_POS
 #define NCC_STREAM_POS 1
 #endif
 constexpr int STREAM_WAVES = NCC_STREAM_WAVES;  // wavefronts per workgroup
-constexpr int STREAM_RS = NCC_STREAM_RS;        // output rows per strip
 constexpr int STREAM_POS = NCC_STREAM_POS;      // output columns per lane
+constexpr int STREAM_WG_PER_CU = 3;             // resident workgroups per CU (168 VGPRs)
+
+template <int WT4, int HT, int RS, bool TALIGN>
+hipError_t launch_stream_rs(const CorrArgs &a, int t, hipStream_t st) {
+    constexpr int NC = STREAM_WAVES * 64 * STREAM_POS;
+    const int ntx = (a.Wo + NC - 1) / NC, nty = (a.Ho + RS - 1) / RS;
+    dim3 grid(xcd_grid(ntx * nty)), block(STREAM_WAVES * 64);
+    if (a.W % 16 == 0 && a.ip % 16 == 0 && ((uintptr_t)a.img & 15) == 0)
+        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, RS, 16, TALIGN>),
+                           grid, block, 0, st, a, t, ntx, nty);
+    else if (a.W % 4 == 0 && a.ip % 4 == 0 && ((uintptr_t)a.img & 3) == 0)
+        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, RS, 4, TALIGN>),
+                           grid, block, 0, st, a, t, ntx, nty);
+    else
+        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, RS, 1, TALIGN>),
+                           grid, block, 0, st, a, t, ntx, nty);
+    return hipGetLastError();
+}
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Strip height: a workgroup streams RS + HT - 1 image rows for RS output
+// rows, one after another, so tall strips waste least on the halo and short
+// ones give more workgroups.  Estimated time ~ (rows per strip) x (waves of
+// workgroups), where fewer workgroups than resident slots still cost one
+// wave; the tallest strip among the cheapest wins.  NCC_STREAM_RS = 16, 32
+// or 64 fixes it instead.
+int stream_rs(int Ho, int ntx, int HT) {
+    if (const char *e = std::getenv("NCC_STREAM_RS")) {
+        const int v = std::atoi(e);
+        if (v == 16 || v == 32 || v == 64) return v;
+    }
+    const double slots = (double)device_cus() * STREAM_WG_PER_CU;
+    int best = 64;
+    double best_cost = 0;
+    for (int rs : {64, 32, 16}) {
+        const double wgs = (double)ntx * ((Ho + rs - 1) / rs);
+        const double cost = (rs + HT - 1) * (wgs > slots ? wgs / slots : 1.0);
+        if (rs == 64 || cost < best_cost) {
+            best = rs;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
 
 template <int WT4, int HT, bool TALIGN>
 hipError_t launch_stream_t(const CorrArgs &a, int t, hipStream_t st) {
+    static_assert(64 % HT == 0 && 32 % HT == 0 && 16 % HT == 0, "strips of whole batches");
     constexpr int NC = STREAM_WAVES * 64 * STREAM_POS;
-    const int ntx = (a.Wo + NC - 1) / NC, nty = (a.Ho + STREAM_RS - 1) / STREAM_RS;
-    dim3 grid(xcd_grid(ntx * nty)), block(STREAM_WAVES * 64);
-    if (a.W % 16 == 0 && ((uintptr_t)a.img & 15) == 0)
-        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, STREAM_RS, 16, TALIGN>),
-                           grid, block, 0, st, a, t, ntx, nty);
-    else if (a.W % 4 == 0 && ((uintptr_t)a.img & 3) == 0)
-        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, STREAM_RS, 4, TALIGN>),
-                           grid, block, 0, st, a, t, ntx, nty);
-    else
-        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, STREAM_RS, 1, TALIGN>),
-                           grid, block, 0, st, a, t, ntx, nty);
-    return hipGetLastError();
+    switch (stream_rs(a.Ho, (a.Wo + NC - 1) / NC, HT)) {
+        case 16: return launch_stream_rs<WT4, HT, 16, TALIGN>(a, t, st);
+        case 32: return launch_stream_rs<WT4, HT, 32, TALIGN>(a, t, st);
+        default: return launch_stream_rs<WT4, HT, 64, TALIGN>(a, t, st);
+    }
 }
 
 template <int WT4, int HT>

@@ -106,9 +106,10 @@ bool sat_fused_from_env() {
     return e && !std::strcmp(e, "fused");
 }
 
-// Builds S and Q on `st`, with `wk` (three-pass scratch) carved by the caller.
-int build_tables(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q, const SatWork &wk,
-                 hipStream_t st) {
+// Builds S and Q of the H x W image with row pitch ip on `st`, with `wk`
+// (three-pass scratch) carved by the caller.
+int build_tables(const uint8_t *img, int W, int H, size_t ip, int64_t *S, int64_t *Q,
+                 const SatWork &wk, hipStream_t st) {
     SatState fs{nullptr, nullptr, 0};
     if (sat_fused_from_env()) {
         void *p = nullptr;
@@ -117,7 +118,7 @@ int build_tables(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q, const
         if (rc != NCC_OK) return rc;
         fs = sat_state_view(p, have);
     }
-    hipError_t e = sat_build_launch(img, W, H, S, Q, wk, fs, st);
+    hipError_t e = sat_build_launch(img, W, H, ip, S, Q, wk, fs, st);
     return e == hipSuccess ? NCC_OK : (e == hipErrorNotSupported ? NCC_EUNSUPPORTED : NCC_EHIP);
 }
 
@@ -140,11 +141,116 @@ Route route_from_env() {
     return Route::Auto;
 }
 
+// One correlation: positions x0 <= x < x0 + w, y0 <= y < y0 + h of the H x W
+// image at img (row pitch ip bytes); output planes of h rows with pitch op
+// elements.  Arguments are validated by the caller; w, h >= 1.
+struct Request {
+    const uint8_t *img;
+    int W, H;
+    size_t ip;
+    const uint8_t *tpl;
+    int wT, hT, nTpl;
+    int x0, y0, w, h;
+    size_t op;
+    int32_t *sums;
+    float *coef;
+};
+
+int correlate_request(const Request &r, hipStream_t st) {
+    const int wT = r.wT, hT = r.hT, nTpl = r.nTpl;
+    const Route route = route_from_env();
+    const bool bank = route == Route::Auto && corr_bank_supported(wT, hT, nTpl);
+    const bool stream_ok = route != Route::Generic && corr_stream_supported(wT, hT);
+    const bool need_tables = !bank && !stream_ok;  // the generic route
+    if (need_tables && !corr_generic_supported(wT, hT)) return NCC_EUNSUPPORTED;
+
+    // The view the kernels see: the rows and columns the positions' windows
+    // cover.  For the streaming kernel on an image with 16-byte aligned rows,
+    // the view starts at the 16-byte boundary at or left of x0 and its width
+    // is rounded up to 16 bytes: x0 - xs and W are multiples of 16, so the
+    // rounded width still ends inside the image row.
+    int xs = 0, Wv = r.w + wT - 1;
+    if (!bank && stream_ok && ((uintptr_t)r.img & 15) == 0 && r.ip % 16 == 0 && r.W % 16 == 0) {
+        xs = r.x0 & 15;
+        Wv = (xs + r.w + wT - 1 + 15) & ~15;
+    }
+    CorrArgs a;
+    a.img = r.img + (size_t)r.y0 * r.ip + (size_t)(r.x0 - xs);
+    a.tpl = r.tpl;
+    a.W = Wv;
+    a.H = r.h + hT - 1;
+    a.wT = wT;
+    a.hT = hT;
+    a.nTpl = nTpl;
+    a.Wo = xs + r.w;
+    a.Ho = r.h;
+    a.xs = xs;
+    a.ip = r.ip;
+    a.op = r.op;
+    a.oplane = (size_t)r.h * r.op;
+    a.rows = nullptr;
+    a.mfma = nullptr;
+    a.stats = nullptr;
+    a.sums = r.sums;
+    a.coef = r.coef;
+
+    // the streaming kernel derives everything from the caller's buffers
+    if (!bank && stream_ok) {
+        for (int t = 0; t < nTpl; t++) {
+            hipError_t e = corr_stream_launch(a, t, st);
+            if (e != hipSuccess) return hip_status(e);
+        }
+        return NCC_OK;
+    }
+
+    // workspace: packed templates, per-template constants, and (generic
+    // route only) the tables of the view and their build scratch
+    const int W = a.W, H = a.H;
+    size_t off_rows = 0;
+    size_t off_mfma = round256(off_rows + tpl_rows_bytes(wT, hT, nTpl));
+    size_t off_stats = round256(off_mfma + (bank ? tpl_mfma_bytes(wT, hT, nTpl) : 0));
+    size_t off_S = round256(off_stats + sizeof(TStat) * (size_t)nTpl);
+    size_t tbl = need_tables ? (size_t)W * H * sizeof(int64_t) : 0;
+    size_t off_Q = round256(off_S + tbl);
+    size_t off_sat = round256(off_Q + tbl);
+    size_t total = off_sat + (need_tables ? sat_work_bytes(W, H) : 0);
+
+    void *ws = nullptr;
+    int rc = get_work(st, total, &ws);
+    if (rc != NCC_OK) return rc;
+    char *base = (char *)ws;
+    a.rows = (const uint32_t *)(base + off_rows);
+    a.mfma = bank ? (const int8_t *)(base + off_mfma) : nullptr;
+    a.stats = (const TStat *)(base + off_stats);
+
+    hipError_t e = tpl_prep_launch(r.tpl, wT, hT, nTpl, (uint32_t *)(base + off_rows),
+                                   bank ? (int8_t *)(base + off_mfma) : nullptr,
+                                   (TStat *)(base + off_stats), st);
+    if (e != hipSuccess) return hip_status(e);
+
+    if (bank) return hip_status(corr_bank_launch(a, st));
+
+    const int64_t *S = nullptr, *Q = nullptr;
+    if (need_tables) {
+        int64_t *Sm = (int64_t *)(base + off_S), *Qm = (int64_t *)(base + off_Q);
+        SatWork wk = sat_work_carve(base + off_sat, W, H);
+        rc = build_tables(a.img, W, H, a.ip, Sm, Qm, wk, st);
+        if (rc != NCC_OK) return rc;
+        S = Sm;
+        Q = Qm;
+    }
+    for (int t = 0; t < nTpl; t++) {
+        e = corr_generic_launch(a, t, S, Q, st);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return NCC_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int ncc_version(void) { return 100; }
+int ncc_version(void) { return 101; }
 
 const char *ncc_strerror(int status) {
     switch (status) {
@@ -168,7 +274,7 @@ int ncc_sat_build(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q, void
     int rc = get_work(st, sat_work_bytes(W, H), &ws);
     if (rc != NCC_OK) return rc;
     SatWork wk = sat_work_carve(ws, W, H);
-    return build_tables(img, W, H, S, Q, wk, st);
+    return build_tables(img, W, H, (size_t)W, S, Q, wk, st);
 }
 
 int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n, int64_t *out,
@@ -191,78 +297,64 @@ int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl, int wT, 
     const unsigned long long planes = (unsigned long long)nTpl + 2;
     if ((unsigned long long)Wo * Ho * planes * 4ull > (1ull << 62)) return NCC_ERANGE;
 
-    const Route route = route_from_env();
-    const bool bank = route == Route::Auto && corr_bank_supported(wT, hT, nTpl);
-    const bool stream_ok = route != Route::Generic && corr_stream_supported(wT, hT);
-    const bool need_tables = !bank && !stream_ok;  // the generic route
-    if (need_tables && !corr_generic_supported(wT, hT)) return NCC_EUNSUPPORTED;
+    Request r;
+    r.img = img;
+    r.W = W;
+    r.H = H;
+    r.ip = (size_t)W;
+    r.tpl = tpl;
+    r.wT = wT;
+    r.hT = hT;
+    r.nTpl = nTpl;
+    r.x0 = 0;
+    r.y0 = 0;
+    r.w = Wo;
+    r.h = Ho;
+    r.op = (size_t)Wo;
+    r.sums = sums_out;
+    r.coef = coef_out;
+    return correlate_request(r, (hipStream_t)stream);
+}
 
-    hipStream_t st = (hipStream_t)stream;
-    CorrArgs a;
-    a.img = img;
-    a.tpl = tpl;
-    a.W = W;
-    a.H = H;
-    a.wT = wT;
-    a.hT = hT;
-    a.nTpl = nTpl;
-    a.Wo = Wo;
-    a.Ho = Ho;
-    a.rows = nullptr;
-    a.mfma = nullptr;
-    a.stats = nullptr;
-    a.sums = sums_out;
-    a.coef = coef_out;
+int ncc_correlate_rect(const uint8_t *img, int W, int H, size_t img_pitch, const uint8_t *tpl,
+                       int wT, int hT, int nTpl, int x0, int y0, int w, int h,
+                       size_t out_pitch, int32_t *sums_out, float *coef_out, void *stream) {
+    if (!img || !tpl) return NCC_EINVAL;
+    if (W < 1 || H < 1 || wT < 1 || hT < 1 || nTpl < 1 || wT > W || hT > H) return NCC_EINVAL;
+    if (img_pitch < (size_t)W || w < 0 || h < 0 || out_pitch < (size_t)w) return NCC_EINVAL;
+    if ((long long)wT * hT > NCC_MAX_TEMPLATE_PIXELS) return NCC_ERANGE;
+    if (img_pitch > (1ull << 40) || (unsigned long long)img_pitch * (unsigned long long)H > (1ull << 48))
+        return NCC_ERANGE;
+    const int Wo = W - wT + 1, Ho = H - hT + 1;
+    if (x0 < 0 || y0 < 0 || x0 > Wo - w || y0 > Ho - h) return NCC_ERANGE;
+    // the view the windows cover obeys the width bound of the tables, and
+    // its table corners stay inside int64
+    if ((long long)w + wT - 1 > NCC_MAX_WIDTH) return NCC_ERANGE;
+    if ((unsigned long long)(w + wT - 1) * (unsigned long long)(h + hT - 1) > (1ull << 40))
+        return NCC_ERANGE;
+    if (out_pitch > NCC_MAX_OUT_PITCH) return NCC_ERANGE;
+    const unsigned long long planes = (unsigned long long)nTpl + 2;
+    if ((unsigned long long)h * out_pitch * planes * 4ull > (1ull << 62)) return NCC_ERANGE;
+    if (w == 0 || h == 0) return NCC_OK;  // no positions: nothing to write
+    if (!coef_out) return NCC_EINVAL;
 
-    // the streaming kernel derives everything from the caller's buffers
-    if (!bank && stream_ok) {
-        for (int t = 0; t < nTpl; t++) {
-            hipError_t e = corr_stream_launch(a, t, st);
-            if (e != hipSuccess) return hip_status(e);
-        }
-        return NCC_OK;
-    }
-
-    // workspace: packed templates, per-template constants, and (generic
-    // route only) the full tables and their build scratch
-    size_t off_rows = 0;
-    size_t off_mfma = round256(off_rows + tpl_rows_bytes(wT, hT, nTpl));
-    size_t off_stats = round256(off_mfma + (bank ? tpl_mfma_bytes(wT, hT, nTpl) : 0));
-    size_t off_S = round256(off_stats + sizeof(TStat) * (size_t)nTpl);
-    size_t tbl = need_tables ? (size_t)W * H * sizeof(int64_t) : 0;
-    size_t off_Q = round256(off_S + tbl);
-    size_t off_sat = round256(off_Q + tbl);
-    size_t total = off_sat + (need_tables ? sat_work_bytes(W, H) : 0);
-
-    void *ws = nullptr;
-    int rc = get_work(st, total, &ws);
-    if (rc != NCC_OK) return rc;
-    char *base = (char *)ws;
-    a.rows = (const uint32_t *)(base + off_rows);
-    a.mfma = bank ? (const int8_t *)(base + off_mfma) : nullptr;
-    a.stats = (const TStat *)(base + off_stats);
-
-    hipError_t e = tpl_prep_launch(tpl, wT, hT, nTpl, (uint32_t *)(base + off_rows),
-                                   bank ? (int8_t *)(base + off_mfma) : nullptr,
-                                   (TStat *)(base + off_stats), st);
-    if (e != hipSuccess) return hip_status(e);
-
-    if (bank) return hip_status(corr_bank_launch(a, st));
-
-    const int64_t *S = nullptr, *Q = nullptr;
-    if (need_tables) {
-        int64_t *Sm = (int64_t *)(base + off_S), *Qm = (int64_t *)(base + off_Q);
-        SatWork wk = sat_work_carve(base + off_sat, W, H);
-        rc = build_tables(img, W, H, Sm, Qm, wk, st);
-        if (rc != NCC_OK) return rc;
-        S = Sm;
-        Q = Qm;
-    }
-    for (int t = 0; t < nTpl; t++) {
-        e = corr_generic_launch(a, t, S, Q, st);
-        if (e != hipSuccess) return hip_status(e);
-    }
-    return NCC_OK;
+    Request r;
+    r.img = img;
+    r.W = W;
+    r.H = H;
+    r.ip = img_pitch;
+    r.tpl = tpl;
+    r.wT = wT;
+    r.hT = hT;
+    r.nTpl = nTpl;
+    r.x0 = x0;
+    r.y0 = y0;
+    r.w = w;
+    r.h = h;
+    r.op = out_pitch;
+    r.sums = sums_out;
+    r.coef = coef_out;
+    return correlate_request(r, (hipStream_t)stream);
 }
 
 void ncc_release(void) {

@@ -47,8 +47,9 @@ SatState sat_state_view(void *base, size_t bytes);
 
 size_t sat_work_bytes(int W, int H);
 SatWork sat_work_carve(void *base, int W, int H);
+// Tables of the H x W image whose row y starts at img + y * ip (ip >= W).
 // fs.ctl == nullptr: the three-pass build; else the single-pass build
-hipError_t sat_build_launch(const uint8_t *img, int W, int H, int64_t *S,
+hipError_t sat_build_launch(const uint8_t *img, int W, int H, size_t ip, int64_t *S,
                             int64_t *Q, const SatWork &wk, const SatState &fs,
                             hipStream_t st);
 
@@ -79,10 +80,21 @@ hipError_t tpl_prep_launch(const uint8_t *tpl, int wT, int hT, int nTpl,
                            hipStream_t st);
 
 // ----------------------------------------------------------- correlation ---
+// A correlation over a view of the image: rows 0..H-1 of W bytes each, row y
+// at img + y * ip, and positions (x, y), xs <= x < Wo, 0 <= y < Ho, whose
+// windows lie inside the view (Wo + wT - 1 <= W, Ho + hT - 1 <= H).  Output
+// of position (x, y) in plane p sits at element p * oplane + y * op + x - xs.
+// Columns below xs are not outputs: a view may start left of the first
+// position so that its rows start on an aligned address (streaming kernel
+// only; the others take xs == 0).
 struct CorrArgs {
     const uint8_t *img;
     const uint8_t *tpl;    // [nTpl][hT][wT] as given by the caller
     int W, H, wT, hT, nTpl, Wo, Ho;
+    int xs;                // first output column of the view
+    size_t ip;             // image row pitch (bytes)
+    size_t op;             // output row pitch (elements)
+    size_t oplane;         // output plane stride (elements)
     const uint32_t *rows;  // packed template rows
     const int8_t *mfma;    // packed bank operands (bank kernel only)
     const TStat *stats;

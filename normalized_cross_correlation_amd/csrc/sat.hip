@@ -34,11 +34,11 @@ constexpr int SAT_SPQ = SAT_QW / SAT_SW;   // strips per row-pass segment
 // the image afterwards (a select, not a branch), so the loads of all rows
 // issue back to back.
 
-// Pixels x, x+1 of row y as the low 16 bits of a dword.  VEC: W even and
-// x even, so x < W implies x + 1 < W.
+// Pixels x, x+1 of row y (at img + y * ip) as the low 16 bits of a dword.
+// VEC: W, ip and x even and img 2-byte aligned, so x < W implies x + 1 < W.
 template <bool VEC>
-__device__ __forceinline__ uint32_t load2(const uint8_t *img, int W, int H, int x, int y) {
-    const uint8_t *row = img + (size_t)min(y, H - 1) * W;
+__device__ __forceinline__ uint32_t load2(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
+    const uint8_t *row = img + (size_t)min(y, H - 1) * ip;
     uint32_t v;
     if (VEC) {
         v = *(const uint16_t *)(row + min(x, W - 2));
@@ -58,10 +58,11 @@ __device__ __forceinline__ uint32_t load2(const uint8_t *img, int W, int H, int 
 // squares stay below 2^31; 8-row column sums of bytes fit 16 bits.
 constexpr int ROWS_PER_WAVE = SAT_BH / 4;
 
-// Bytes x .. x+15 of row y.  VEC: W % 16 == 0 and x % 16 == 0.
+// Bytes x .. x+15 of row y.  VEC: W, ip and x multiples of 16, img 16-byte
+// aligned.
 template <bool VEC>
-__device__ __forceinline__ uint4 load16(const uint8_t *img, int W, int H, int x, int y) {
-    const uint8_t *row = img + (size_t)min(y, H - 1) * W;
+__device__ __forceinline__ uint4 load16(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
+    const uint8_t *row = img + (size_t)min(y, H - 1) * ip;
     uint4 v;
     if (VEC) {
         v = *(const uint4 *)(row + min(x, W - 16));
@@ -89,7 +90,7 @@ __device__ __forceinline__ uint32_t oct_sum_u32(uint32_t x) {
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void sat_rows(const uint8_t *__restrict__ img, int W, int H,
+__global__ __launch_bounds__(256) void sat_rows(const uint8_t *__restrict__ img, int W, int H, size_t ip,
                                                 SatWork wk) {
     const int q = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void sat_rows(const uint8_t *__restrict__ img,
     const int y0 = b * SAT_BH + ROWS_PER_WAVE * w;
     uint4 px[ROWS_PER_WAVE];
 #pragma unroll
-    for (int r = 0; r < ROWS_PER_WAVE; r++) px[r] = load16<VEC>(img, W, H, x, y0 + r);
+    for (int r = 0; r < ROWS_PER_WAVE; r++) px[r] = load16<VEC>(img, ip, W, H, x, y0 + r);
 
     __shared__ uint32_t stot[2][SAT_BH][SAT_SPQ];   // strip sums of each row
     __shared__ uint32_t part[2][4][SAT_QW];         // [table][wave][column] 8-row sums
@@ -304,10 +305,10 @@ template <bool VEC>
 struct BandIn {
     uint32_t px[WAVE_ROWS];
     uint32_t lc1, lc2;
-    __device__ __forceinline__ void load(const uint8_t *img, int W, int H, const SatWork &wk,
+    __device__ __forceinline__ void load(const uint8_t *img, size_t ip, int W, int H, const SatWork &wk,
                                          int s, int x, int y0, int l) {
 #pragma unroll
-        for (int r = 0; r < WAVE_ROWS; r++) px[r] = load2<VEC>(img, W, H, x, y0 + r);
+        for (int r = 0; r < WAVE_ROWS; r++) px[r] = load2<VEC>(img, ip, W, H, x, y0 + r);
         const size_t r1 = (size_t)min(y0 + (l & (WAVE_ROWS - 1)), H - 1), r2 = (size_t)H + r1;
         lc1 = wk.lrowl[r1 * wk.nStrips + s];
         lc2 = wk.lrowl[r2 * wk.nStrips + s];
@@ -320,7 +321,7 @@ struct BandIn {
 };
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__ img, int W, int H,
+__global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__ img, int W, int H, size_t ip,
                                                      SatWork wk, int64_t *__restrict__ S,
                                                      int64_t *__restrict__ Q) {
     const int nTy = (wk.nBands + SAT_SUB - 1) / SAT_SUB;
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
         s2b = tp2[xb];
     }
     BandIn<VEC> cur, nxt;
-    cur.load(img, W, H, wk, s, x, ytile + w * WAVE_ROWS, l);
+    cur.load(img, ip, W, H, wk, s, x, ytile + w * WAVE_ROWS, l);
 
     __shared__ uint64_t part[2][4][4][64];  // [band parity][wave][value][lane]
     typedef long long v2l __attribute__((ext_vector_type(2)));
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
             c2b += R2b[r];
         }
         // the next band's inputs are in flight while this band is stored
-        if (k + 1 < SAT_SUB) nxt.load(img, W, H, wk, s, x, y0 + SAT_BH, l);
+        if (k + 1 < SAT_SUB) nxt.load(img, ip, W, H, wk, s, x, y0 + SAT_BH, l);
 
         const int pb = k & 1;
         part[pb][w][0][l] = c1a;
@@ -494,7 +495,7 @@ __device__ __forceinline__ uint64_t look_back(const uint64_t *p, size_t stride, 
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img, int W, int H,
+__global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img, int W, int H, size_t ip,
                                                  SatState fs, int nS, int nTiles,
                                                  int64_t *__restrict__ S, int64_t *__restrict__ Q) {
     constexpr int TR = SAT_BH * SAT_FSUB;  // tile rows
@@ -543,7 +544,7 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
         uint32_t px[WAVE_ROWS];
 #pragma unroll
         for (int r = 0; r < WAVE_ROWS; r++)
-            px[r] = load2<VEC>(img, W, H, x, ytile + SAT_BH * k + WAVE_ROWS * w + r);
+            px[r] = load2<VEC>(img, ip, W, H, x, ytile + SAT_BH * k + WAVE_ROWS * w + r);
 #pragma unroll
         for (int r = 0; r < WAVE_ROWS; r++) {
             const uint32_t b0 = px[r] & 0xffu, b1 = (px[r] >> 8) & 0xffu;
@@ -602,7 +603,7 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
     const bool pair = VEC && x + 1 < W;
     uint32_t pc[WAVE_ROWS], pn[WAVE_ROWS];
 #pragma unroll
-    for (int r = 0; r < WAVE_ROWS; r++) pc[r] = load2<VEC>(img, W, H, x, ytile + WAVE_ROWS * w + r);
+    for (int r = 0; r < WAVE_ROWS; r++) pc[r] = load2<VEC>(img, ip, W, H, x, ytile + WAVE_ROWS * w + r);
 #pragma unroll
     for (int k = 0; k < SAT_FSUB; k++) {
         const int yb = ytile + SAT_BH * k;
@@ -631,7 +632,7 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
         }
         if (k + 1 < SAT_FSUB) {
 #pragma unroll
-            for (int r = 0; r < WAVE_ROWS; r++) pn[r] = load2<VEC>(img, W, H, x, y0 + SAT_BH + r);
+            for (int r = 0; r < WAVE_ROWS; r++) pn[r] = load2<VEC>(img, ip, W, H, x, y0 + SAT_BH + r);
         }
         const int pb = k & 1;
         part[pb][w][0][l] = d1a;
@@ -739,35 +740,35 @@ SatState sat_state_view(void *base, size_t bytes) {
     return fs;
 }
 
-hipError_t sat_build_launch(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q,
+hipError_t sat_build_launch(const uint8_t *img, int W, int H, size_t ip, int64_t *S, int64_t *Q,
                             const SatWork &wk, const SatState &fs, hipStream_t st) {
     if (fs.ctl) {
         const int nS = (W + SAT_FW - 1) / SAT_FW;
         const int nG = (H + SAT_BH * SAT_FSUB - 1) / (SAT_BH * SAT_FSUB);
         const int nTiles = nS * nG;
         if (nTiles > fs.capTiles) return hipErrorInvalidValue;
-        const bool vec = (W % 2 == 0) && (((uintptr_t)img & 1) == 0) &&
+        const bool vec = (W % 2 == 0) && (ip % 2 == 0) && (((uintptr_t)img & 1) == 0) &&
                          (((uintptr_t)S & 15) == 0) && (((uintptr_t)Q & 15) == 0);
         if (vec)
-            hipLaunchKernelGGL(sat_fused<true>, dim3(nTiles), dim3(256), 0, st, img, W, H, fs, nS,
+            hipLaunchKernelGGL(sat_fused<true>, dim3(nTiles), dim3(256), 0, st, img, W, H, ip, fs, nS,
                                nTiles, S, Q);
         else
-            hipLaunchKernelGGL(sat_fused<false>, dim3(nTiles), dim3(256), 0, st, img, W, H, fs, nS,
+            hipLaunchKernelGGL(sat_fused<false>, dim3(nTiles), dim3(256), 0, st, img, W, H, ip, fs, nS,
                                nTiles, S, Q);
         return hipGetLastError();
     }
     // aligned 16-byte image rows (and band rows) for the row pass; even
     // widths and 16-byte table rows for the paired loads and stores of the
     // downsweep
-    const bool rvec = (W % 16 == 0) && (((uintptr_t)img & 15) == 0);
-    const bool dvec = (W % 2 == 0) && (((uintptr_t)img & 1) == 0) &&
+    const bool rvec = (W % 16 == 0) && (ip % 16 == 0) && (((uintptr_t)img & 15) == 0);
+    const bool dvec = (W % 2 == 0) && (ip % 2 == 0) && (((uintptr_t)img & 1) == 0) &&
                       (((uintptr_t)S & 15) == 0) && (((uintptr_t)Q & 15) == 0);
     dim3 block(256);
     dim3 rgrid(wk.nSeg, wk.nBands);
     if (rvec)
-        hipLaunchKernelGGL(sat_rows<true>, rgrid, block, 0, st, img, W, H, wk);
+        hipLaunchKernelGGL(sat_rows<true>, rgrid, block, 0, st, img, W, H, ip, wk);
     else
-        hipLaunchKernelGGL(sat_rows<false>, rgrid, block, 0, st, img, W, H, wk);
+        hipLaunchKernelGGL(sat_rows<false>, rgrid, block, 0, st, img, W, H, ip, wk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sat_top, dim3(2 * ((W + TOP_COLS - 1) / TOP_COLS)), block, 0, st, W, wk);
@@ -775,9 +776,9 @@ hipError_t sat_build_launch(const uint8_t *img, int W, int H, int64_t *S, int64_
     if (e != hipSuccess) return e;
     dim3 grid(xcd_grid(wk.nStrips * ((wk.nBands + SAT_SUB - 1) / SAT_SUB)));
     if (dvec)
-        hipLaunchKernelGGL(sat_downsweep<true>, grid, block, 0, st, img, W, H, wk, S, Q);
+        hipLaunchKernelGGL(sat_downsweep<true>, grid, block, 0, st, img, W, H, ip, wk, S, Q);
     else
-        hipLaunchKernelGGL(sat_downsweep<false>, grid, block, 0, st, img, W, H, wk, S, Q);
+        hipLaunchKernelGGL(sat_downsweep<false>, grid, block, 0, st, img, W, H, ip, wk, S, Q);
     return hipGetLastError();
 }
 

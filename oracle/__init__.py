@@ -204,6 +204,29 @@ def correlate_at(img, tpl, pos, S=None, Q=None, nthreads: int = 0):
     return coef, sums
 
 
+def correlate_rect(img, tpl, x0: int, y0: int, w: int, h: int, nthreads: int = 0):
+    """Values at the positions x0..x0+w-1 by y0..y0+h-1 only: the sample
+    program's rectangle of positions ("Image in shared memory", the offsets
+    of corrShared_kernel), each window inside the image.
+
+    Returns (coef float32 [nTpl][h][w], sums int64 [2+nTpl][h][w]), the
+    per-position values of correlate_at laid out as the rectangle.
+    """
+    img = _u8_2d(img)
+    tpl = _templates(tpl)
+    H, W = img.shape
+    nT, hT, wT = tpl.shape
+    if w < 0 or h < 0 or x0 < 0 or y0 < 0 or x0 + w > W - wT + 1 or y0 + h > H - hT + 1:
+        raise ValueError("rectangle outside the valid positions")
+    ys, xs = np.meshgrid(np.arange(y0, y0 + h), np.arange(x0, x0 + w), indexing="ij")
+    pos = np.stack([xs.ravel(), ys.ravel()], axis=1)
+    if pos.shape[0] == 0:
+        return np.zeros((nT, h, w), np.float32), np.zeros((2 + nT, h, w), np.int64)
+    coef, sums = correlate_at(img, tpl, pos, nthreads=nthreads)
+    return (np.ascontiguousarray(coef.T.reshape(nT, h, w)),
+            np.ascontiguousarray(sums.T.reshape(2 + nT, h, w)))
+
+
 def threads(nthreads: int = 0) -> int:
     """Threads the oracle's OpenMP regions use for a given request."""
     return int(_load().oracle_threads(nthreads))

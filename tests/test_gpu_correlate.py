@@ -55,6 +55,23 @@ def test_single_template_routes(oracle_mod, rname, H, W, hT, wT, kind, seed):
     _compare(oracle_mod, c["img"], c["tpl"], d, route_name=rname)
 
 
+@pytest.mark.parametrize("rs", ["16", "32", "64"])
+@pytest.mark.parametrize("H,W,hT,wT,seed", [
+    (16, 40, 16, 16, 51),     # one output row
+    (47, 300, 16, 16, 52),    # 32 rows: one 32-row strip or two 16-row strips
+    (143, 529, 16, 15, 53),   # ragged tail at every strip height
+    (96, 256, 16, 16, 54),    # 81 rows
+])
+def test_stream_strip_heights(oracle_mod, monkeypatch, rs, H, W, hT, wT, seed):
+    """The streaming kernel at each strip height (chosen per launch from the
+    output size; fixed here)."""
+    d = need_gpu()
+    monkeypatch.setenv("NCC_STREAM_RS", rs)
+    announce("correlate stream rs=%s %dx%d tpl %dx%d" % (rs, H, W, hT, wT))
+    c = synth.random_case(seed, H, W, hT, wT, nTpl=1, kind="smooth")
+    _compare(oracle_mod, c["img"], c["tpl"], d)
+
+
 @pytest.mark.parametrize("H,W,hT,wT,seed", [
     (50, 60, 1, 1, 11), (33, 47, 3, 3, 12), (70, 90, 17, 17, 13),
     (100, 100, 32, 32, 14), (64, 200, 5, 31, 15), (120, 80, 40, 9, 16),

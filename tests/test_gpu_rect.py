@@ -1,0 +1,181 @@
+"""GPU parity of ncc_correlate_rect (a rectangle of positions read in place
+from a row-strided image, written to row-strided output) against the oracle.
+
+Sums bit for bit, coefficients within 1e-5 absolute; the padding between w
+and the output pitch is never written; a rectangle covering every position
+gives exactly ncc_correlate's output.  Each route is taken: the streaming
+kernel (on 16-byte aligned image rows it starts its view at the 16-byte
+boundary left of x0), the generic kernel on the rectangle's own tables
+(three-pass and single-pass builds) and the matrix-core bank.
+"""
+import numpy as np
+import pytest
+
+from normalized_cross_correlation_amd import synth
+from tests.gpu_util import COEF_ATOL, announce, dev, host, need_gpu, route
+
+pytestmark = pytest.mark.gpu
+
+
+def _strided_image(img, d, pad_left, pad_right, pad_top=2):
+    """img placed inside a larger device buffer: a view with row pitch
+    pad_left + W + pad_right whose base is pad_left bytes into a row."""
+    import torch
+    H, W = img.shape
+    big = np.full((H + pad_top + 1, pad_left + W + pad_right), 77, np.uint8)
+    big[pad_top:pad_top + H, pad_left:pad_left + W] = img
+    t = torch.from_numpy(big).to(d)
+    v = t[pad_top:pad_top + H, pad_left:pad_left + W]
+    assert v.stride(0) == pad_left + W + pad_right
+    return v
+
+
+def _check(oracle_mod, img, tpl, d, x0, y0, w, h, out_pitch=None, img_dev=None, want_sums=True):
+    import torch
+    import normalized_cross_correlation_amd as ncc
+    n = 1 if tpl.ndim == 2 else tpl.shape[0]
+    op = out_pitch or w
+    cbuf = torch.full((n, h, op), float("nan"), dtype=torch.float32, device=d)
+    sbuf = torch.full((2 + n, h, op), -7, dtype=torch.int32, device=d)
+    coef, sums = ncc.correlate_rect(img_dev if img_dev is not None else dev(img, d),
+                                    dev(tpl, d), x0, y0, w, h,
+                                    coef=cbuf[:, :, :w], sums=sbuf[:, :, :w] if want_sums else None)
+    torch.cuda.synchronize()
+    co, so = oracle_mod.correlate_rect(img, tpl, x0, y0, w, h)
+    if want_sums:
+        np.testing.assert_array_equal(host(sums).astype(np.int64), so)
+    err = np.abs(host(coef).astype(np.float64) - co.astype(np.float64))
+    assert err.max() <= COEF_ATOL, "max |coef - oracle| = %g" % err.max()
+    if op > w:
+        assert np.isnan(host(cbuf)[:, :, w:]).all(), "coef padding written"
+        assert (host(sbuf)[:, :, w:] == -7).all(), "sums padding written"
+    if not want_sums:
+        assert (host(sbuf) == -7).all()
+    return host(coef)
+
+
+# x0, y0, w, h on a 200 x 320 image (valid positions 305 x 185 for 16 x 16)
+RECTS = [
+    (0, 0, 1, 1), (7, 3, 37, 20), (5, 0, 300, 9), (16, 30, 64, 150),
+    (305 - 40, 185 - 70, 40, 70),  # touches the right and bottom edges
+    (1, 1, 304, 184), (300, 100, 5, 1),
+]
+
+
+@pytest.mark.parametrize("x0,y0,w,h", RECTS)
+@pytest.mark.parametrize("layout", ["dense16", "pitched16", "pitched_odd"])
+def test_stream_rects(oracle_mod, layout, x0, y0, w, h):
+    """16 x 16 template: the streaming kernel, on 16-byte aligned rows (its
+    view starts left of x0) and on rows at odd addresses and pitch."""
+    d = need_gpu()
+    announce("rect stream %s (%d,%d) %dx%d" % (layout, x0, y0, w, h))
+    c = synth.random_case(200 + x0 + y0, 200, 320, 16, 16, nTpl=1, kind="smooth")
+    img = c["img"]
+    if layout == "dense16":
+        iv = None
+    elif layout == "pitched16":
+        iv = _strided_image(img, d, 32, 48)
+    else:
+        iv = _strided_image(img, d, 5, 2)
+    _check(oracle_mod, img, c["tpl"], d, x0, y0, w, h, out_pitch=w + 3, img_dev=iv)
+
+
+@pytest.mark.parametrize("x0,y0,w,h", [(0, 0, 5, 5), (3, 9, 57, 41), (60, 2, 71, 80)])
+@pytest.mark.parametrize("sat_path", ["passes", "fused"])
+def test_generic_rects(oracle_mod, monkeypatch, sat_path, x0, y0, w, h):
+    """9 x 11 template: the generic kernel on the tables of the rectangle's
+    view, from a pitched image."""
+    d = need_gpu()
+    monkeypatch.setenv("NCC_SAT_PATH", sat_path)
+    announce("rect generic sat=%s (%d,%d) %dx%d" % (sat_path, x0, y0, w, h))
+    c = synth.random_case(300 + x0, 130, 145, 11, 9, nTpl=2, kind="uniform")
+    iv = _strided_image(c["img"], d, 3, 9)
+    _check(oracle_mod, c["img"], c["tpl"], d, x0, y0, w, h, out_pitch=w + 1, img_dev=iv)
+
+
+def test_generic_route_forced_16x16(oracle_mod):
+    d = need_gpu()
+    announce("rect generic forced 16x16")
+    c = synth.random_case(310, 150, 200, 16, 16, nTpl=1, kind="smooth")
+    with route("generic"):
+        _check(oracle_mod, c["img"], c["tpl"], d, 13, 17, 150, 100, out_pitch=160)
+
+
+@pytest.mark.parametrize("x0,y0,w,h", [(0, 0, 64, 16), (5, 3, 70, 33), (100, 50, 1, 1),
+                                       (200 - 16 + 1 - 90, 180 - 16 + 1 - 45, 90, 45)])
+@pytest.mark.parametrize("n,hT,wT", [(20, 16, 16), (16, 8, 12)])
+def test_bank_rects(oracle_mod, n, hT, wT, x0, y0, w, h):
+    """Template banks on the matrix cores, pitched output with 256-byte rows."""
+    d = need_gpu()
+    announce("rect bank n=%d %dx%d (%d,%d) %dx%d" % (n, hT, wT, x0, y0, w, h))
+    c = synth.random_case(400 + n + x0, 180, 200, hT, wT, nTpl=n, kind="smooth")
+    if x0 + w > 200 - wT + 1 or y0 + h > 180 - hT + 1:
+        pytest.skip("rectangle outside this template's valid positions")
+    _check(oracle_mod, c["img"], c["tpl"], d, x0, y0, w, h, out_pitch=(w + 63) // 64 * 64)
+
+
+@pytest.mark.parametrize("n,hT,wT", [(1, 16, 16), (12, 16, 16), (1, 7, 5)])
+def test_full_rect_equals_correlate(n, hT, wT):
+    """The rectangle of every position, dense output: bit for bit
+    ncc_correlate."""
+    import torch
+    import normalized_cross_correlation_amd as ncc
+    d = need_gpu()
+    announce("rect full == correlate n=%d %dx%d" % (n, hT, wT))
+    c = synth.random_case(500 + n, 190, 260, hT, wT, nTpl=n, kind="smooth")
+    img, tpl = dev(c["img"], d), dev(c["tpl"], d)
+    ec, es = ncc.correlate(img, tpl, want_sums=True)
+    Ho, Wo = 190 - hT + 1, 260 - wT + 1
+    rc, rs = ncc.correlate_rect(img, tpl, 0, 0, Wo, Ho, want_sums=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(rc), host(ec))
+    np.testing.assert_array_equal(host(rs), host(es))
+
+
+def test_empty_and_rejected():
+    import torch
+    import normalized_cross_correlation_amd as ncc
+    d = need_gpu()
+    announce("rect empty / rejected")
+    img = torch.zeros((40, 50), dtype=torch.uint8, device=d)
+    tpl = torch.ones((4, 4), dtype=torch.uint8, device=d)
+    coef, sums = ncc.correlate_rect(img, tpl, 3, 3, 0, 5, want_sums=True)
+    assert tuple(coef.shape) == (1, 5, 0) and tuple(sums.shape) == (3, 5, 0)
+    with pytest.raises(ncc.NCCError) as e:
+        ncc.correlate_rect(img, tpl, 45, 0, 3, 1)  # last window past the edge
+    assert e.value.code == -2
+    with pytest.raises(ncc.NCCError):
+        ncc.correlate_rect(img, tpl, 0, 36, 1, 2)
+
+
+def test_full_size_local_searches(oracle_mod):
+    """4096 x 4096 box-blurred noise, 16 x 16 template cut from it: search
+    rectangles around the cut (aligned and unaligned offsets) find it with
+    gamma = 1, and sampled positions match the oracle."""
+    import torch
+    import normalized_cross_correlation_amd as ncc
+    d = need_gpu()
+    announce("rect full-size local searches 4096^2")
+    wk = synth.make("headline")
+    img, tpl = wk["img"], wk["tpl"]
+    (cx, cy), = wk["cut_xy"]
+    di, dt = dev(img, d), dev(tpl, d)
+    rng = np.random.default_rng(17)
+    Ho, Wo = img.shape[0] - 15, img.shape[1] - 15
+    for dx, dy, w, h in [(100, 77, 256, 200), (16, 16, 33, 33), (1000, 900, 1931, 1500)]:
+        # the rectangle around the cut, shifted to lie inside the valid positions
+        x0 = min(max(cx - dx, 0), Wo - w)
+        y0 = min(max(cy - dy, 0), Ho - h)
+        coef, sums = ncc.correlate_rect(di, dt, x0, y0, w, h, want_sums=True)
+        torch.cuda.synchronize()
+        c = host(coef)[0]
+        s = host(sums)
+        assert abs(c[cy - y0, cx - x0] - 1.0) <= COEF_ATOL
+        assert np.unravel_index(np.argmax(c), c.shape) == (cy - y0, cx - x0)
+        pick = np.stack([rng.integers(0, w, 300), rng.integers(0, h, 300)], axis=1)
+        pos = pick + np.array([x0, y0])
+        oc, osums = oracle_mod.correlate_at(img, tpl, pos)
+        got_c = c[pick[:, 1], pick[:, 0]]
+        got_s = s[:, pick[:, 1], pick[:, 0]].T.astype(np.int64)
+        np.testing.assert_array_equal(got_s, osums)
+        assert np.abs(got_c.astype(np.float64) - oc[:, 0]).max() <= COEF_ATOL

@@ -183,3 +183,38 @@ def test_coefficient_formula_pieces(oracle_mod):
 def test_template_stats(oracle_mod):
     t = np.array([[1, 2], [3, 4]], np.uint8)
     assert oracle_mod.template_stats(t) == (10, 30, 4 * 30 - 100)
+
+
+@pytest.mark.parametrize("x0,y0,w,h", [(0, 0, 1, 1), (3, 5, 9, 4), (10, 2, 8, 13), (0, 0, 18, 15)])
+def test_correlate_rect_pinned(oracle_mod, x0, y0, w, h):
+    """The sample program's rectangle of positions (offsets into the image,
+    "Image in shared memory"): SumIT against scipy's valid correlation of the
+    rectangle's image region, SumI / SumISq against direct window sums, the
+    coefficient against numpy.corrcoef, and the whole against the full map."""
+    c = synth.random_case(91, 22, 25, 6, 8, nTpl=2, kind="smooth")
+    img, tpl = c["img"], c["tpl"]
+    coef, sums = oracle_mod.correlate_rect(img, tpl, x0, y0, w, h)
+    assert coef.shape == (2, h, w) and sums.shape == (4, h, w)
+    region = img[y0:y0 + h + 5, x0:x0 + w + 7].astype(np.int64)
+    win = _windows(region, 6, 8)
+    np.testing.assert_array_equal(sums[0], win.sum(axis=(2, 3)))
+    np.testing.assert_array_equal(sums[1], (win * win).sum(axis=(2, 3)))
+    for t in range(2):
+        np.testing.assert_array_equal(sums[2 + t], correlate2d(region, tpl[t].astype(np.int64),
+                                                               mode="valid"))
+        np.testing.assert_allclose(coef[t], _pearson_map(region, tpl[t]), atol=1e-5, rtol=0)
+    full_c, full_s = oracle_mod.correlate(img, tpl)
+    np.testing.assert_array_equal(coef, full_c[:, y0:y0 + h, x0:x0 + w])
+    np.testing.assert_array_equal(sums, full_s[:, y0:y0 + h, x0:x0 + w])
+
+
+def test_correlate_rect_bounds(oracle_mod):
+    c = synth.random_case(92, 12, 14, 3, 4, nTpl=1, kind="uniform")
+    Ho, Wo = 10, 11
+    coef, sums = oracle_mod.correlate_rect(c["img"], c["tpl"], Wo - 2, Ho - 3, 2, 3)
+    assert coef.shape == (1, 3, 2)
+    e_c, e_s = oracle_mod.correlate_rect(c["img"], c["tpl"], 4, 4, 0, 3)
+    assert e_c.shape == (1, 3, 0) and e_s.shape == (3, 3, 0)
+    for x0, y0, w, h in [(Wo - 1, 0, 2, 1), (0, Ho - 2, 1, 3), (-1, 0, 1, 1), (0, 0, -1, 1)]:
+        with pytest.raises(ValueError):
+            oracle_mod.correlate_rect(c["img"], c["tpl"], x0, y0, w, h)
