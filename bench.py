@@ -128,6 +128,18 @@ def cpu_baseline(img, tpl, budget_s=12.0):
     }
 
 
+RECTS = (("local_256", 256, 256), ("sub_2048", 2048, 2048))
+
+
+def rect_origin(cut_xy, rw, rh, Wo, Ho):
+    """A rw x rh search rectangle around the template's origin, inside the
+    valid positions, at an odd (not 16-byte aligned) offset."""
+    cx, cy = cut_xy
+    x0 = min(min(max(cx - rw // 2, 0), Wo - rw) | 1, Wo - rw)
+    y0 = min(min(max(cy - rh // 2, 0), Ho - rh) | 1, Ho - rh)
+    return x0, y0
+
+
 def run_loop(args, L, sh, d):
     """Repeats one call type; the workload of each is the one the JSON line
     reports for it."""
@@ -138,7 +150,8 @@ def run_loop(args, L, sh, d):
         dst = torch.empty_like(src)
         fns = [lambda: dst.copy_(src)]
     else:
-        name = {"sat": "sat", "box": "sat", "corr": "headline", "bank": "bank"}[args.loop]
+        name = {"sat": "sat", "box": "sat", "corr": "headline", "rect": "headline",
+                "bank": "bank"}[args.loop]
         w = synth.make(name)
         img = torch.from_numpy(w["img"]).to(d)
         H, W = img.shape
@@ -153,6 +166,16 @@ def run_loop(args, L, sh, d):
                 fns = [lambda: L.ncc_sat_build(img.data_ptr(), W, H, S.data_ptr(), Q.data_ptr(), sh)]
             else:
                 fns = [lambda: L.ncc_box(S.data_ptr(), W, H, rects.data_ptr(), n, out.data_ptr(), sh)]
+        elif args.loop == "rect":
+            tpl = torch.from_numpy(w["tpl"]).to(d)
+            _, hT, wT = tpl.shape
+            fns = []
+            for _name, rw, rh in RECTS:
+                x0, y0 = rect_origin(w["cut_xy"][0], rw, rh, W - wT + 1, H - hT + 1)
+                rc_ = torch.empty((1, rh, rw), dtype=torch.float32, device=d)
+                fns.append(lambda x0=x0, y0=y0, rw=rw, rh=rh, rc_=rc_: L.ncc_correlate_rect(
+                    img.data_ptr(), W, H, W, tpl.data_ptr(), wT, hT, 1, x0, y0, rw, rh, rw, None,
+                    rc_.data_ptr(), sh))
         else:
             tpl = torch.from_numpy(w["tpl"]).to(d)
             nt, hT, wT = tpl.shape
@@ -179,7 +202,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="time only the headline step (used under the profiler)")
-    ap.add_argument("--loop", choices=["sat", "corr", "bank", "box", "copy"],
+    ap.add_argument("--loop", choices=["sat", "corr", "bank", "box", "rect", "copy"],
                     help="profiling aid: run one call type --steps times after --warmup and "
                          "exit without the JSON line (copy: a plain 256 MiB device copy, the "
                          "reference for scaling HBM byte counters)")
@@ -371,10 +394,8 @@ def main():
         # and a large sub-image, both at offsets that are not 16-byte aligned
         (cx, cy), = w["cut_xy"]
         rect_out = {"workload": "4096x4096 headline image, 16x16 template: ncc_correlate_rect"}
-        for name, (rw, rh) in (("local_256", (256, 256)), ("sub_2048", (2048, 2048))):
-            x0 = min(max(cx - rw // 2, 0), Wo - rw) | 1
-            y0 = min(max(cy - rh // 2, 0), Ho - rh) | 1
-            x0, y0 = min(x0, Wo - rw), min(y0, Ho - rh)
+        for name, rw, rh in RECTS:
+            x0, y0 = rect_origin((cx, cy), rw, rh, Wo, Ho)
             rcoef = torch.empty((1, rh, rw), dtype=torch.float32, device=d)
             prc = rcoef.data_ptr()
 
