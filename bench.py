@@ -61,6 +61,19 @@ def _traffic(kernel_key, src_names):
     return t.get("bytes_per_launch")
 
 
+def ramp(fns, seconds=0.1):
+    """Untimed steps for `seconds` of wall time.  The GPU's clocks rise under
+    sustained load: the first ~30 ms of this workload run up to ~16% slower
+    than the steady state, far longer than a few warm-up steps take."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+
+
 def time_steps(fns, steps, warmup):
     """Wall seconds of `steps` steps (one step = each callable once, in order,
     back to back on the device) after `warmup` untimed steps, bracketed by a
@@ -78,22 +91,25 @@ def time_steps(fns, steps, warmup):
     return time.perf_counter() - t0
 
 
-def time_each(fns, steps, stream):
-    """Mean ms of each callable from HIP events recorded on `stream` around
-    every call, over `steps` more steps.  An event between two calls makes
-    the second wait for the first to drain, so this pass times the calls, not
-    the step."""
+def time_each(fns, calls, stream):
+    """Mean ms per call of each callable: `calls` back-to-back calls of it
+    between two HIP events recorded on `stream`.  (An event after every call
+    would add the event's own ~6 us of barrier and timestamp per call: the
+    kernel durations rocprofv3 reports agree with back-to-back blocks, not
+    with per-call events.)"""
     import torch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for s in range(steps):
-        ev[s][0].record(stream)
-        for i, f in enumerate(fns):
+    out = []
+    for f in fns:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        f()
+        e0.record(stream)
+        for _ in range(calls):
             f()
-            ev[s][i + 1].record(stream)
-    torch.cuda.synchronize()
-    return [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
-            for i in range(len(fns))]
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / calls)
+    return out
 
 
 def cpu_baseline(img, tpl, budget_s=12.0):
@@ -182,6 +198,8 @@ def run_loop(args, L, sh, d):
             coef = torch.empty((nt, H - hT + 1, W - wT + 1), dtype=torch.float32, device=d)
             fns = [lambda: L.ncc_correlate(img.data_ptr(), W, H, tpl.data_ptr(), wT, hT, nt, None,
                                            coef.data_ptr(), sh)]
+    if args.ramp > 0:
+        ramp(fns, args.ramp)
     for _ in range(args.warmup):
         for f in fns:
             f()
@@ -206,6 +224,9 @@ def main():
                     help="profiling aid: run one call type --steps times after --warmup and "
                          "exit without the JSON line (copy: a plain 256 MiB device copy, the "
                          "reference for scaling HBM byte counters)")
+    ap.add_argument("--ramp", type=float, default=0.1,
+                    help="seconds of untimed calls before the warm-up (clock ramp); the "
+                         "counter passes of the profiling loops use 0")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -249,6 +270,7 @@ def main():
         if rc:
             raise RuntimeError("ncc_correlate: %d" % rc)
 
+    ramp([sat, corr])
     wall = time_steps([sat, corr], args.steps, args.warmup)
     ms_step = wall / args.steps * 1e3
     # per-call durations (for the roofline and components) from a second pass
@@ -322,7 +344,6 @@ def main():
             assert L.ncc_box(pS, W, H, pr, n, pb1, sh) == 0
             assert L.ncc_box(pQ, W, H, pr, n, pb2, sh) == 0
 
-        time_steps([sat2, boxes], 0, 3)
         t_b, t_q = time_each([sat2, boxes], 20, stream)
         rate = sat_bytes / (t_b * 1e-3) / 1e9
         # the single-pass (look-back) build of the same tables, for comparison
@@ -350,7 +371,7 @@ def main():
         def bank():
             assert L.ncc_correlate(pbi, W, H, pbt, wT, hT, nb, None, pbc, sh) == 0
 
-        time_steps([bank], 0, 2)
+        ramp([bank], 0.05)
         t_k, = time_each([bank], 10, stream)
         bcoeffs = nb * coeffs
         out_bytes = bcoeffs * 4 + H * W
@@ -377,7 +398,6 @@ def main():
             assert L.ncc_correlate_rect(pbi, W, H, W, pbt, wT, hT, nb, 0, 0, Wo, Ho, op, None,
                                         ppc, sh) == 0
 
-        time_steps([bank_pitched], 0, 2)
         t_kp, = time_each([bank_pitched], 10, stream)
         for (x, y), t in zip(wb["cut_xy"], range(nb)):
             assert abs(float(pcoef[t, y, x]) - 1.0) <= 1e-5
@@ -403,8 +423,8 @@ def main():
                 assert L.ncc_correlate_rect(pi, W, H, W, pt, wT, hT, 1, x0, y0, rw, rh, rw, None,
                                             prc, sh) == 0
 
-            time_steps([rect], 0, 3)
-            t_r, = time_each([rect], 20, stream)
+            ramp([rect], 0.03)
+            t_r, = time_each([rect], 50, stream)
             assert abs(float(rcoef[0, cy - y0, cx - x0]) - 1.0) <= 1e-5
             rect_out[name] = {"origin": [x0, y0], "size": [rw, rh], "us": round(t_r * 1e3, 2),
                               "Gcoeff/s": round(rw * rh / (t_r * 1e-3) / 1e9, 1)}
