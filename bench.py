@@ -112,6 +112,46 @@ def time_each(fns, calls, stream):
     return out
 
 
+def measured_peaks(stream, d):
+    """Compute units and clock from the device, the dot4 issue peak they
+    imply, and the rates three microbenchmarks reach (libncc_peaks.so):
+    1 GiB of 16-byte-per-lane stores in the table build's pattern (rows of
+    32 KiB, tiles of 1 KiB x 32 rows, 8 rows per wavefront), 8
+    independent dot4 chains per lane at 4 wavefronts per SIMD, and 8
+    independent 16x16x64 int8 MFMA chains per wavefront at 4 wavefronts per
+    SIMD."""
+    import ctypes
+    import torch
+    from normalized_cross_correlation_amd import build as nb
+    P = ctypes.CDLL(nb.PEAKS_LIB)
+    V, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    P.ncc_peak_props.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I)]
+    P.ncc_peak_write.argtypes = [V, Z, I, V]
+    P.ncc_peak_dot4.argtypes = [V, I, I, V]
+    P.ncc_peak_mfma_i8.argtypes = [V, I, I, V]
+    sh = stream.cuda_stream
+    cus, clk = I(), I()
+    assert P.ncc_peak_props(ctypes.byref(cus), ctypes.byref(clk)) == 0
+    cus, ghz = cus.value, clk.value / 1e6
+    nbytes = 1 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=d)
+    t_w, = time_each([lambda: P.ncc_peak_write(buf.data_ptr(), nbytes, 32768, sh)], 20, stream)
+    del buf
+    blocks, it_d, it_m = cus * 4, 4096, 1024
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=d)
+    t_d, = time_each([lambda: P.ncc_peak_dot4(out.data_ptr(), blocks, it_d, sh)], 10, stream)
+    t_m, = time_each([lambda: P.ncc_peak_mfma_i8(out.data_ptr(), blocks, it_m, sh)], 10, stream)
+    dot4_ops = blocks * 256 * 8 * it_d * 4 * 2           # lanes x dot4 x MACs x 2
+    mfma_ops = blocks * 4 * 8 * it_m * 16 * 16 * 64 * 2  # waves x MFMAs x MACs x 2
+    return {
+        "compute_units": cus, "clock_GHz": round(ghz, 3),
+        "dot4_TOP/s_from_clock": round(cus * 4 * 16 * 4 * 2 * ghz / 1e3, 1),
+        "write_GB/s": round(nbytes / (t_w * 1e-3) / 1e9, 1),
+        "dot4_TOP/s": round(dot4_ops / (t_d * 1e-3) / 1e12, 1),
+        "int8_mfma_TOP/s": round(mfma_ops / (t_m * 1e-3) / 1e12, 1),
+        "method": "rates of libncc_peaks.so microbenchmarks (events around back-to-back launches)"}
+
+
 def cpu_baseline(img, tpl, budget_s=12.0):
     """The oracle (plain C, OpenMP over output rows) on the first R output rows
     of the headline image, R sized so the run takes about budget_s."""
@@ -329,6 +369,14 @@ def main():
 
     # ------------------------------------------------ other workloads ----
     if not args.no_extra:
+        pk = measured_peaks(stream, d)
+        out["measured_peaks"] = pk
+        if roof["unit"] == "GB/s":
+            roof["peak_measured"] = pk["write_GB/s"]
+        else:
+            roof["peak_measured"] = pk["dot4_TOP/s"]
+        roof["frac_of_measured"] = round(roof["achieved"] / roof["peak_measured"], 4)
+
         ws = synth.make("sat")
         simg = torch.from_numpy(ws["img"]).to(d)
         rects = torch.from_numpy(ws["rects"]).to(d)

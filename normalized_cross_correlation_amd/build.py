@@ -1,4 +1,5 @@
-"""Builds libncc.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Builds libncc.so (the HIP kernels and the C ABI) for gfx950 with hipcc, and
+libncc_peaks.so (hardware-rate microbenchmarks that only the benchmark loads).
 
 Usage: ``python -m normalized_cross_correlation_amd.build`` or ``build()``.
 Objects go to ``_build/`` at the repository root; the library lands next to
@@ -17,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libncc.so")
+PEAKS_LIB = os.path.join(PKG, "libncc_peaks.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -27,6 +29,7 @@ CFLAGS = [
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 SOURCES = ["sat.hip", "tpl.hip", "corr.hip", "bank.hip", "ncc_api.hip"]
+PEAKS_SOURCES = ["peaks.hip"]
 
 
 def _compile(src: str) -> str:
@@ -43,18 +46,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PEAKS_LIB)
     return LIB
 
 

@@ -115,3 +115,17 @@ def test_correlate_rect_empty_is_noop(L):
     assert _rect(L, x0=36, w=0, op=0, coef=None) == OK  # empty at the right edge
     assert _rect(L, h=0, w=3, op=3, coef=None) == OK
     assert _rect(L, x0=40, w=0, op=0, coef=None) == ERANGE  # still validated
+
+
+def test_peaks_library_exports():
+    """The benchmark's microbenchmark library (not part of the C ABI)."""
+    from normalized_cross_correlation_amd import build
+    if not os.path.exists(build.PEAKS_LIB):
+        build.build()
+    P = ctypes.CDLL(build.PEAKS_LIB)
+    for name in ("ncc_peak_props", "ncc_peak_write", "ncc_peak_dot4", "ncc_peak_mfma_i8"):
+        assert hasattr(P, name), name
+    P.ncc_peak_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    # shapes it cannot tile are refused before any launch
+    assert P.ncc_peak_write(FAKE, 1 << 20, 1000, None) == -1
+    assert P.ncc_peak_write(None, 1 << 20, 1024, None) == -1
