@@ -65,9 +65,12 @@ __device__ __forceinline__ void store_sum(int32_t *p, int32_t v) {
 
 // ------------------------------------------------------------- streaming --
 // Registers of one lane of the streaming kernel, which owns POS adjacent
-// output columns.
-template <int WT4, int HT, int POS>
+// output columns.  MASK: the template's last dword is partial (wT < 4 WT4);
+// WSUM: the window sums are written too.
+template <int WT4_, int HT_, int POS_, bool MASK_, bool WSUM_>
 struct StreamState {
+    static constexpr int WT4 = WT4_, HT = HT_, POS = POS_;
+    static constexpr bool MASK = MASK_, WSUM = WSUM_;
     uint32_t tp[HT][WT4];      // template rows (zero-padded dwords)
     uint32_t acc[POS][HT];     // SumIT rings: slot (row mod HT) of the output row
     uint32_t pI[POS][HT];      // running column sums of HT rows ago
@@ -80,7 +83,7 @@ struct StreamState {
     int32_t *s0, *s1, *s2;     // ... and its sums planes
     uint32_t off;              // + this offset (elements): the lane's first column of the
                                //   next finished row
-    bool wsum, wfirst;         // sums wanted; SumI / SumISq planes written by this call
+    bool wfirst;               // SumI / SumISq planes written by this call
     bool pairs;                // wave-uniform: every lane's POS columns are distinct
     int yrel;                  // output row (relative to the strip) finished next
 };
@@ -98,10 +101,10 @@ typedef float f2u __attribute__((ext_vector_type(2), aligned(4)));
 typedef int i2u __attribute__((ext_vector_type(2), aligned(4)));
 
 // nI = -SumI (mod 2^32), as the running sums give it.
-template <int WT4, int HT, int POS>
-__device__ __forceinline__ float stream_coef(const StreamState<WT4, HT, POS> &st, uint32_t nI,
-                                             uint32_t sumISq, uint32_t sumIT) {
-    if (HT * 4 * WT4 <= 256) {
+template <class ST>
+__device__ __forceinline__ float stream_coef(const ST &st, uint32_t nI, uint32_t sumISq,
+                                             uint32_t sumIT) {
+    if (ST::HT * 4 * ST::WT4 <= 256) {
         // K*SumIT < 2^24 and SumISq < 2^24 (unsigned 24-bit products); SumI,
         // SumT < 2^16 (signed 24-bit); |num| <= K^2 * 127.5^2 < 2^31: exact mod 2^32
         const int32_t num = __mul24((int)st.sumT, (int)nI) + (int32_t)__umul24(st.K, sumIT);
@@ -120,10 +123,13 @@ __device__ __forceinline__ float stream_coef(const StreamState<WT4, HT, POS> &st
 // rows, where template rows j > Q land above the strip and are skipped;
 // PHASE 2: the HT rows after the strip's last output row starts, where
 // template rows j <= Q land below the strip and are skipped (the windows of
-// the strip's last HT-1 output rows still end here); PHASE 1: all.
-template <int WT4, int HT, int POS, int Q, int PHASE>
-__device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
-                                           const uint32_t (&d)[WT4 + 1], int rowsOut, uint32_t op) {
+// the strip's last HT-1 output rows still end here); PHASE 1: all.  CHECK:
+// the strip may end before this row's output (a strip cut by the image
+// bottom); op: output row pitch in elements.
+template <class ST, int Q, int PHASE, bool CHECK>
+__device__ __forceinline__ void stream_row(ST &st, const uint32_t (&d)[ST::WT4 + 1], int rowsOut,
+                                           uint32_t op) {
+    constexpr int WT4 = ST::WT4, HT = ST::HT, POS = ST::POS;
     uint32_t v[POS][WT4];
 #pragma unroll
     for (int p = 0; p < POS; p++)
@@ -134,7 +140,7 @@ __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
         uint32_t hs = 0, hs2 = 0;
 #pragma unroll
         for (int k = 0; k < WT4; k++) {
-            const uint32_t vm = (k == WT4 - 1) ? (v[p][k] & st.mlast) : v[p][k];
+            const uint32_t vm = (ST::MASK && k == WT4 - 1) ? (v[p][k] & st.mlast) : v[p][k];
             hs = dot4u(vm, 0x01010101u, hs);
             hs2 = dot4u(vm, vm, hs2);
         }
@@ -177,30 +183,29 @@ __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
     if (PHASE == 0 && Q != HT - 1) return;  // no window ends here yet
     // every lane holds real columns (lanes past the last one repeat it), so
     // only the wave-uniform row test guards the stores
-    if (st.yrel < rowsOut) {
+    if (!CHECK || st.yrel < rowsOut) {
         float g[POS];
 #pragma unroll
         for (int p = 0; p < POS; p++) g[p] = stream_coef(st, nI[p], sumISq[p], sumIT[p]);
         if (POS == 2 && st.pairs) {
-            __builtin_nontemporal_store((f2u){g[0], g[POS - 1]}, (f2u *)(st.out + st.off));
-            if (st.wsum) {
+            __builtin_nontemporal_store((f2u){g[0], g[POS - 1]}, (f2u *)st.out + st.off);
+            if (ST::WSUM) {
                 if (st.wfirst) {
                     __builtin_nontemporal_store((i2u){-(int)nI[0], -(int)nI[POS - 1]},
-                                                (i2u *)(st.s0 + st.off));
+                                                (i2u *)st.s0 + st.off);
                     __builtin_nontemporal_store((i2u){(int)sumISq[0], (int)sumISq[POS - 1]},
-                                                (i2u *)(st.s1 + st.off));
+                                                (i2u *)st.s1 + st.off);
                 }
                 __builtin_nontemporal_store((i2u){(int)sumIT[0], (int)sumIT[POS - 1]},
-                                            (i2u *)(st.s2 + st.off));
+                                            (i2u *)st.s2 + st.off);
             }
         } else {
             // edge lanes: column p of this lane is min(first + p, Wo - 1)
 #pragma unroll
             for (int p = 0; p < POS; p++) {
-                const int dp = (int)(st.sh[p] - st.sh[0]);
-                const uint32_t o = st.off + dp;
+                const uint32_t o = st.off + (st.sh[p] - st.sh[0]);
                 store_coef(st.out + o, g[p]);
-                if (st.wsum) {
+                if (ST::WSUM) {
                     if (st.wfirst) {
                         store_sum(st.s0 + o, -(int32_t)nI[p]);
                         store_sum(st.s1 + o, (int32_t)sumISq[p]);
@@ -216,24 +221,25 @@ __device__ __forceinline__ void stream_row(StreamState<WT4, HT, POS> &st,
 
 // Rows Q .. HT-1 of a batch; the LDS reads of row Q+1 are issued before row
 // Q's arithmetic.
-template <int WT4, int HT, int POS, int Q, int PHASE>
-__device__ __forceinline__ void stream_rows(StreamState<WT4, HT, POS> &st, const uint32_t *rowbase,
-                                            int pitch, uint32_t (&d)[WT4 + 1], int rowsOut,
+template <class ST, int Q, int PHASE, bool CHECK>
+__device__ __forceinline__ void stream_rows(ST &st, const uint32_t *rowbase, int pitch,
+                                            uint32_t (&d)[ST::WT4 + 1], int rowsOut,
                                             uint32_t op) {
+    constexpr int WT4 = ST::WT4, HT = ST::HT;
     uint32_t dn[WT4 + 1];
     if constexpr (Q + 1 < HT) {
 #pragma unroll
         for (int k = 0; k <= WT4; k++) dn[k] = rowbase[(Q + 1) * pitch + k];
     }
-    stream_row<WT4, HT, POS, Q, PHASE>(st, d, rowsOut, op);
+    stream_row<ST, Q, PHASE, CHECK>(st, d, rowsOut, op);
     if constexpr (Q + 1 < HT) {
 #pragma unroll
         for (int k = 0; k <= WT4; k++) d[k] = dn[k];
-        stream_rows<WT4, HT, POS, Q + 1, PHASE>(st, rowbase, pitch, d, rowsOut, op);
+        stream_rows<ST, Q + 1, PHASE, CHECK>(st, rowbase, pitch, d, rowsOut, op);
     }
 }
 
-template <int WT4, int HT, int POS, int WAVES, int RS, int ALIGN, bool TALIGN>
+template <int WT4, int HT, int POS, int WAVES, int RS, int ALIGN, bool TALIGN, bool WSUM>
 #ifndef NCC_STREAM_WPE
 #define NCC_STREAM_WPE 3
 #endif
@@ -255,7 +261,9 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
     const int x0 = (tix % ntx) * NC, y0 = (tix / ntx) * RS;
     const int rowsOut = min(RS, a.Ho - y0);
 
-    StreamState<WT4, HT, POS> st;
+    // a template row-aligned in whole dwords (TALIGN) needs no mask
+    typedef StreamState<WT4, HT, POS, !TALIGN, WSUM> ST;
+    ST st;
     // the lane's columns; lanes past the last output column compute (and
     // store) that column again, lanes before the first one (xs) the first
     const int xf = x0 + POS * tid;
@@ -308,10 +316,9 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
     const size_t o0 = (size_t)y0 * a.op;
     st.off = (uint32_t)(xa - a.xs);
     st.out = a.coef + (size_t)t * plane + o0;
-    st.wsum = a.sums != nullptr;
     st.wfirst = t == 0;
-    // only dereferenced when st.wsum (and st.wfirst for s0, s1)
-    int32_t *sb = st.wsum ? a.sums : (int32_t *)a.coef;
+    // only dereferenced when WSUM (and st.wfirst for s0, s1)
+    int32_t *sb = WSUM ? a.sums : (int32_t *)a.coef;
     st.s0 = sb + o0;
     st.s1 = sb + plane + o0;
     st.s2 = sb + (size_t)(2 + t) * plane + o0;
@@ -385,7 +392,9 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
     if (nb > 1) fetch(1);
 #pragma unroll
     for (int k = 0; k <= WT4; k++) d[k] = rowbase0[k];
-    stream_rows<WT4, HT, POS, 0, 0>(st, rowbase0, PITCH, d, rowsOut, (uint32_t)a.op);
+    // the first batch's one output (its last row) is the strip's row 0
+    const uint32_t op = (uint32_t)a.op;
+    stream_rows<ST, 0, 0, false>(st, rowbase0, PITCH, d, rowsOut, op);
     if (nb > 1) put(1);
     __syncthreads();
     // full batches
@@ -394,7 +403,7 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
         const uint32_t *rowbase = rowbase0 + (bt & 1) * HT * PITCH;
 #pragma unroll
         for (int k = 0; k <= WT4; k++) d[k] = rowbase[k];
-        stream_rows<WT4, HT, POS, 0, 1>(st, rowbase, PITCH, d, rowsOut, (uint32_t)a.op);
+        stream_rows<ST, 0, 1, true>(st, rowbase, PITCH, d, rowsOut, op);
         if (bt + 1 < nb) put(bt + 1);
         __syncthreads();
     }
@@ -403,7 +412,7 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
         const uint32_t *rowbase = rowbase0 + ((nb - 1) & 1) * HT * PITCH;
 #pragma unroll
         for (int k = 0; k <= WT4; k++) d[k] = rowbase[k];
-        stream_rows<WT4, HT, POS, 0, 2>(st, rowbase, PITCH, d, rowsOut, (uint32_t)a.op);
+        stream_rows<ST, 0, 2, true>(st, rowbase, PITCH, d, rowsOut, op);
     }
 }
 
@@ -528,19 +537,19 @@ constexpr int STREAM_WAVES = NCC_STREAM_WAVES;  // wavefronts per workgroup
 constexpr int STREAM_POS = NCC_STREAM_POS;      // output columns per lane
 constexpr int STREAM_WG_PER_CU = 3;             // resident workgroups per CU (168 VGPRs)
 
-template <int WT4, int HT, int RS, bool TALIGN>
+template <int WT4, int HT, int RS, bool TALIGN, bool WSUM>
 hipError_t launch_stream_rs(const CorrArgs &a, int t, hipStream_t st) {
     constexpr int NC = STREAM_WAVES * 64 * STREAM_POS;
     const int ntx = (a.Wo + NC - 1) / NC, nty = (a.Ho + RS - 1) / RS;
     dim3 grid(xcd_grid(ntx * nty)), block(STREAM_WAVES * 64);
     if (a.W % 16 == 0 && a.ip % 16 == 0 && ((uintptr_t)a.img & 15) == 0)
-        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, RS, 16, TALIGN>),
+        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, RS, 16, TALIGN, WSUM>),
                            grid, block, 0, st, a, t, ntx, nty);
     else if (a.W % 4 == 0 && a.ip % 4 == 0 && ((uintptr_t)a.img & 3) == 0)
-        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, RS, 4, TALIGN>),
+        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, RS, 4, TALIGN, WSUM>),
                            grid, block, 0, st, a, t, ntx, nty);
     else
-        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, RS, 1, TALIGN>),
+        hipLaunchKernelGGL((corr_stream<WT4, HT, STREAM_POS, STREAM_WAVES, RS, 1, TALIGN, WSUM>),
                            grid, block, 0, st, a, t, ntx, nty);
     return hipGetLastError();
 }
@@ -588,10 +597,18 @@ template <int WT4, int HT, bool TALIGN>
 hipError_t launch_stream_t(const CorrArgs &a, int t, hipStream_t st) {
     static_assert(64 % HT == 0 && 32 % HT == 0 && 16 % HT == 0, "strips of whole batches");
     constexpr int NC = STREAM_WAVES * 64 * STREAM_POS;
-    switch (stream_rs(a.Ho, (a.Wo + NC - 1) / NC, HT)) {
-        case 16: return launch_stream_rs<WT4, HT, 16, TALIGN>(a, t, st);
-        case 32: return launch_stream_rs<WT4, HT, 32, TALIGN>(a, t, st);
-        default: return launch_stream_rs<WT4, HT, 64, TALIGN>(a, t, st);
+    const int rs = stream_rs(a.Ho, (a.Wo + NC - 1) / NC, HT);
+    if (a.sums) {
+        switch (rs) {
+            case 16: return launch_stream_rs<WT4, HT, 16, TALIGN, true>(a, t, st);
+            case 32: return launch_stream_rs<WT4, HT, 32, TALIGN, true>(a, t, st);
+            default: return launch_stream_rs<WT4, HT, 64, TALIGN, true>(a, t, st);
+        }
+    }
+    switch (rs) {
+        case 16: return launch_stream_rs<WT4, HT, 16, TALIGN, false>(a, t, st);
+        case 32: return launch_stream_rs<WT4, HT, 32, TALIGN, false>(a, t, st);
+        default: return launch_stream_rs<WT4, HT, 64, TALIGN, false>(a, t, st);
     }
 }
 
