@@ -199,6 +199,7 @@ def rect_origin(cut_xy, rw, rh, Wo, Ho):
 def run_loop(args, L, sh, d):
     """Repeats one call type; the workload of each is the one the JSON line
     reports for it."""
+    import numpy as np
     import torch
     from normalized_cross_correlation_amd import synth
     if args.loop == "copy":
@@ -207,7 +208,7 @@ def run_loop(args, L, sh, d):
         fns = [lambda: dst.copy_(src)]
     else:
         name = {"sat": "sat", "box": "sat", "corr": "headline", "rect": "headline",
-                "bank": "bank"}[args.loop]
+                "large": "headline", "bank": "bank"}[args.loop]
         w = synth.make(name)
         img = torch.from_numpy(w["img"]).to(d)
         H, W = img.shape
@@ -222,6 +223,12 @@ def run_loop(args, L, sh, d):
                 fns = [lambda: L.ncc_sat_build(img.data_ptr(), W, H, S.data_ptr(), Q.data_ptr(), sh)]
             else:
                 fns = [lambda: L.ncc_box(S.data_ptr(), W, H, rects.data_ptr(), n, out.data_ptr(), sh)]
+        elif args.loop == "large":
+            # a 128 x 128 template: the FFT numerator route
+            ltpl = torch.from_numpy(np.ascontiguousarray(w["img"][100:228, 200:328])[None]).to(d)
+            lcoef = torch.empty((1, H - 127, W - 127), dtype=torch.float32, device=d)
+            fns = [lambda: L.ncc_correlate(img.data_ptr(), W, H, ltpl.data_ptr(), 128, 128, 1, None,
+                                           lcoef.data_ptr(), sh)]
         elif args.loop == "rect":
             tpl = torch.from_numpy(w["tpl"]).to(d)
             _, hT, wT = tpl.shape
@@ -260,7 +267,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="time only the headline step (used under the profiler)")
-    ap.add_argument("--loop", choices=["sat", "corr", "bank", "box", "rect", "copy"],
+    ap.add_argument("--loop", choices=["sat", "corr", "bank", "box", "rect", "large", "copy"],
                     help="profiling aid: run one call type --steps times after --warmup and "
                          "exit without the JSON line (copy: a plain 256 MiB device copy, the "
                          "reference for scaling HBM byte counters)")
@@ -477,6 +484,33 @@ def main():
             rect_out[name] = {"origin": [x0, y0], "size": [rw, rh], "us": round(t_r * 1e3, 2),
                               "Gcoeff/s": round(rw * rh / (t_r * 1e-3) / 1e9, 1)}
         out["rect_workload"] = rect_out
+
+        # large templates on the headline image: the FFT numerator the library
+        # picks for them, against the direct generic kernel forced
+        lt_out = {"workload": "4096x4096 headline image, one t x t template cut from it: "
+                              "ncc_correlate (table build + FFT numerator), against the direct "
+                              "generic kernel (NCC_CORR_PATH=generic)"}
+        for t in (64, 128):
+            ltpl = torch.from_numpy(np.ascontiguousarray(img_np[100:100 + t, 200:200 + t])[None]).to(d)
+            lcoef = torch.empty((1, H - t + 1, W - t + 1), dtype=torch.float32, device=d)
+            plt, plc = ltpl.data_ptr(), lcoef.data_ptr()
+
+            def large(t=t, plt=plt, plc=plc):
+                assert L.ncc_correlate(pi, W, H, plt, t, t, 1, None, plc, sh) == 0
+
+            t_auto, = time_each([large], 10, stream)
+            assert abs(float(lcoef[0, 100, 200]) - 1.0) <= 1e-5
+            os.environ["NCC_CORR_PATH"] = "generic"
+            try:
+                t_dir, = time_each([large], 3, stream)
+            finally:
+                os.environ.pop("NCC_CORR_PATH", None)
+            n_co = (H - t + 1) * (W - t + 1)
+            lt_out["t%d" % t] = {"fft_ms": round(t_auto, 4), "direct_ms": round(t_dir, 4),
+                                 "Gcoeff/s": round(n_co / (t_auto * 1e-3) / 1e9, 1),
+                                 "T_MAC/s_equivalent": round(n_co * t * t / (t_auto * 1e-3) / 1e12, 1)}
+            del lcoef
+        out["large_template_workload"] = lt_out
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(img_np, tpl_np[0])

@@ -114,7 +114,12 @@ int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n,
  * strip for the specialised kernels, the full int64 tables of ncc_sat_build
  * in the workspace otherwise).  A bank (nTpl > 1) of templates with at most
  * 16 rows of at most 16 pixels runs SumIT as an int8 matrix-core
- * contraction; other shapes run per template on the vector units.
+ * contraction; other shapes run per template on the vector units, or, for
+ * large templates (where it is estimated faster; about 48 x 48 and up on a
+ * 4096 x 4096 image), as a product of 2-D Fourier transforms in double
+ * precision whose result is rounded to the integer SumIT it equals (the
+ * "FFT numerator" section 15.8 names; images whose padded transform exceeds
+ * 8192 x 8192 always run the direct kernel).
  *
  * Errors: NCC_EINVAL (null img/tpl/coef_out, W or H < 1, wT or hT < 1,
  * wT > W, hT > H, nTpl < 1), NCC_ERANGE (W > NCC_MAX_WIDTH,

@@ -131,14 +131,31 @@ int hip_status(hipError_t e) {
 }
 
 // Which correlation route to take; NCC_CORR_PATH selects one explicitly
-// ("generic", "single" for one template at a time, default "auto").
-enum class Route { Auto, Generic, Single };
+// ("generic", "fft", "single" for one template at a time, default "auto").
+enum class Route { Auto, Generic, Fft, Single };
 Route route_from_env() {
     const char *e = std::getenv("NCC_CORR_PATH");
     if (!e) return Route::Auto;
     if (!std::strcmp(e, "generic")) return Route::Generic;
+    if (!std::strcmp(e, "fft")) return Route::Fft;
     if (!std::strcmp(e, "single")) return Route::Single;
     return Route::Auto;
+}
+
+// Whether a template that no specialised kernel takes goes through the FFT
+// numerator rather than the direct generic kernel: estimated times from the
+// measured rates of both on this part (direct: ~55 T MAC/s for large
+// templates; FFT: ~10 spectrum passes per template and 3 for the image, each
+// pass moving the spectrum twice at ~5.3 TB/s).  At 4096 x 4096 the two
+// meet near a 48 x 48 template (0.73 ms each).
+bool fft_chosen(Route route, int Wv, int Hv, int Wo, int Ho, int wT, int hT, int nTpl) {
+    if (!corr_fft_supported(Wv, Hv)) return false;
+    if (route == Route::Fft) return true;
+    if (route != Route::Auto) return false;
+    const double spec = (double)corr_fft_bytes(Wv, Hv) / 3.0;
+    const double t_fft = 20e-6 + (3.0 + 10.0 * nTpl) * 2.0 * spec / 5.3e12;
+    const double t_direct = (double)nTpl * Wo * (double)Ho * wT * (double)hT / 55e12;
+    return t_fft < t_direct;
 }
 
 // One correlation: positions x0 <= x < x0 + w, y0 <= y < y0 + h of the H x W
@@ -160,9 +177,12 @@ int correlate_request(const Request &r, hipStream_t st) {
     const int wT = r.wT, hT = r.hT, nTpl = r.nTpl;
     const Route route = route_from_env();
     const bool bank = route == Route::Auto && corr_bank_supported(wT, hT, nTpl);
-    const bool stream_ok = route != Route::Generic && corr_stream_supported(wT, hT);
-    const bool need_tables = !bank && !stream_ok;  // the generic route
+    const bool stream_ok =
+        (route == Route::Auto || route == Route::Single) && corr_stream_supported(wT, hT);
+    const bool need_tables = !bank && !stream_ok;  // the generic and FFT routes
     if (need_tables && !corr_generic_supported(wT, hT)) return NCC_EUNSUPPORTED;
+    const bool fft = need_tables && fft_chosen(route, r.w + wT - 1, r.h + hT - 1, r.w, r.h, wT,
+                                               hT, nTpl);
 
     // The view the kernels see: the rows and columns the positions' windows
     // cover.  For the streaming kernel on an image with 16-byte aligned rows,
@@ -213,7 +233,8 @@ int correlate_request(const Request &r, hipStream_t st) {
     size_t tbl = need_tables ? (size_t)W * H * sizeof(int64_t) : 0;
     size_t off_Q = round256(off_S + tbl);
     size_t off_sat = round256(off_Q + tbl);
-    size_t total = off_sat + (need_tables ? sat_work_bytes(W, H) : 0);
+    size_t off_fft = round256(off_sat + (need_tables ? sat_work_bytes(W, H) : 0));
+    size_t total = off_fft + (fft ? corr_fft_bytes(W, H) : 0);
 
     void *ws = nullptr;
     int rc = get_work(st, total, &ws);
@@ -239,6 +260,7 @@ int correlate_request(const Request &r, hipStream_t st) {
         S = Sm;
         Q = Qm;
     }
+    if (fft) return hip_status(corr_fft_launch(a, S, Q, base + off_fft, st));
     for (int t = 0; t < nTpl; t++) {
         e = corr_generic_launch(a, t, S, Q, st);
         if (e != hipSuccess) return hip_status(e);

@@ -113,6 +113,15 @@ bool corr_generic_supported(int wT, int hT);
 hipError_t corr_generic_launch(const CorrArgs &a, int t, const int64_t *S,
                                const int64_t *Q, hipStream_t st);
 
+// SumIT by 2-D FFT in double precision (large templates), SumI and SumISq
+// from the full int64 tables S, Q of the view.  Supported while the view's
+// padded transform sizes stay within 8192 x 8192; needs corr_fft_bytes(W, H)
+// of workspace (the spectra and the twiddle table).
+bool corr_fft_supported(int W, int H);
+size_t corr_fft_bytes(int W, int H);
+hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q, void *work,
+                           hipStream_t st);
+
 // Template bank on the int8 matrix cores.
 bool corr_bank_supported(int wT, int hT, int nTpl);
 hipError_t corr_bank_launch(const CorrArgs &a, hipStream_t st);
