@@ -30,7 +30,9 @@ namespace {
 
 constexpr int TW_LOG = 14;
 constexpr int TWN = 1 << TW_LOG;  // twiddle table: exp(-2 pi i k / TWN), k < TWN
-constexpr int FFT_T = 256;        // threads per workgroup
+constexpr int FFT_T = 256;        // threads per workgroup of the column passes
+constexpr int ROW_T = 1024;       // ... of the row transforms (one row per workgroup: enough
+                                  //   wavefronts per CU at up to 160 KB of LDS each)
 constexpr int FFT_TB = 32;        // columns per workgroup in the column passes
 constexpr int FFT_MAX_LOG = 13;   // transform lengths up to 8192 per dimension
 
@@ -50,6 +52,33 @@ __device__ __forceinline__ double2 scaled(double2 a, double s) { return make_dou
 // W_N^x = exp(-2 pi i x / N) for N = 2^e, 0 <= x < N.
 __device__ __forceinline__ double2 tw_at(const double2 *__restrict__ tw, int x, int e) {
     return tw[x << (TW_LOG - e)];
+}
+
+// Twiddles from the global table.
+struct TwGlobal {
+    const double2 *__restrict__ tw;
+    __device__ __forceinline__ double2 operator()(int x, int e) const { return tw_at(tw, x, e); }
+};
+
+// Twiddles from a quarter table in LDS: q[r] = W_NT^r for r < NT/4 (NT =
+// 2^eNT), and W_NT^(r + m NT/4) = (-i)^m W_NT^r.
+struct TwLds {
+    const double2 *q;
+    int eNT;
+    __device__ __forceinline__ double2 operator()(int x, int e) const {
+        const int y = x << (eNT - e);
+        const int m = y >> (eNT - 2), r = y & ((1 << (eNT - 2)) - 1);
+        const double2 w = q[r];
+        // (-i)^m w: m = 1 -> (w.y, -w.x), 2 -> -w, 3 -> (-w.y, w.x)
+        const double re = (m & 1) ? w.y : w.x, im = (m & 1) ? w.x : w.y;
+        const double sr = (m < 2) ? 1.0 : -1.0, si = (m == 0 || m == 3) ? 1.0 : -1.0;
+        return make_double2(sr * re, si * im);
+    }
+};
+
+// Fills q[r] = W_NT^r, r < NT/4, from the global table.
+__device__ __forceinline__ void load_quarter(double2 *q, int eNT, const double2 *__restrict__ tw) {
+    for (int r = threadIdx.x; r < (1 << (eNT - 2)); r += blockDim.x) q[r] = tw_at(tw, r, eNT);
 }
 
 // Position of frequency k after a length-2^e decimation-in-frequency
@@ -91,16 +120,17 @@ __device__ __forceinline__ int fft_freq(int p, int e) {
 // sequences of length N = 2^e held in LDS as buf[n * B + b]: decimation in
 // frequency, a radix-2 stage first when e is odd, then radix-4 stages; the
 // output of frequency k sits at position fft_pos(k, e).  Ends with a barrier.
-__device__ void lds_dif(double2 *buf, int e, int B, const double2 *__restrict__ tw) {
+template <class TW>
+__device__ void lds_dif(double2 *buf, int e, int B, const TW tw) {
     const int N = 1 << e;
     int L = N, eL = e;
     if (e & 1) {
         const int s = N >> 1;
-        for (int idx = threadIdx.x; idx < s * B; idx += FFT_T) {
+        for (int idx = threadIdx.x; idx < s * B; idx += blockDim.x) {
             const int j = idx / B, b = idx - j * B;
             const double2 a0 = buf[j * B + b], a1 = buf[(j + s) * B + b];
             buf[j * B + b] = cadd(a0, a1);
-            buf[(j + s) * B + b] = cmul(csub(a0, a1), tw_at(tw, j, e));
+            buf[(j + s) * B + b] = cmul(csub(a0, a1), tw(j, e));
         }
         __syncthreads();
         L = s;
@@ -108,7 +138,7 @@ __device__ void lds_dif(double2 *buf, int e, int B, const double2 *__restrict__ 
     }
     for (; L >= 4; L >>= 2, eL -= 2) {
         const int s = L >> 2;
-        for (int idx = threadIdx.x; idx < (N >> 2) * B; idx += FFT_T) {
+        for (int idx = threadIdx.x; idx < (N >> 2) * B; idx += blockDim.x) {
             const int bf = idx / B, b = idx - bf * B;
             const int g = bf / s, j = bf - g * s;
             const int i0 = (g * L + j) * B + b;
@@ -117,9 +147,9 @@ __device__ void lds_dif(double2 *buf, int e, int B, const double2 *__restrict__ 
             const double2 t0 = cadd(a0, a2), t1 = csub(a0, a2), t2 = cadd(a1, a3),
                           t3 = mul_mi(csub(a1, a3));
             buf[i0] = cadd(t0, t2);
-            buf[i0 + s * B] = cmul(cadd(t1, t3), tw_at(tw, j, eL));
-            buf[i0 + 2 * s * B] = cmul(csub(t0, t2), tw_at(tw, 2 * j, eL));
-            buf[i0 + 3 * s * B] = cmul(csub(t1, t3), tw_at(tw, 3 * j, eL));
+            buf[i0 + s * B] = cmul(cadd(t1, t3), tw(j, eL));
+            buf[i0 + 2 * s * B] = cmul(csub(t0, t2), tw(2 * j, eL));
+            buf[i0 + 3 * s * B] = cmul(csub(t1, t3), tw(3 * j, eL));
         }
         __syncthreads();
     }
@@ -128,19 +158,20 @@ __device__ void lds_dif(double2 *buf, int e, int B, const double2 *__restrict__ 
 // The exact reverse of lds_dif with conjugate twiddles: input at positions
 // fft_pos(k, e), output in natural order, N times the inverse DFT.  Ends
 // with a barrier.
-__device__ void lds_dit_inv(double2 *buf, int e, int B, const double2 *__restrict__ tw) {
+template <class TW>
+__device__ void lds_dit_inv(double2 *buf, int e, int B, const TW tw) {
     const int N = 1 << e;
     const int eTop = (e & 1) ? e - 1 : e;
     for (int eL = 2; eL <= eTop; eL += 2) {
         const int L = 1 << eL, s = L >> 2;
-        for (int idx = threadIdx.x; idx < (N >> 2) * B; idx += FFT_T) {
+        for (int idx = threadIdx.x; idx < (N >> 2) * B; idx += blockDim.x) {
             const int bf = idx / B, b = idx - bf * B;
             const int g = bf / s, j = bf - g * s;
             const int i0 = (g * L + j) * B + b;
             const double2 x0 = buf[i0];
-            const double2 x1 = cmulc(buf[i0 + s * B], tw_at(tw, j, eL));
-            const double2 x2 = cmulc(buf[i0 + 2 * s * B], tw_at(tw, 2 * j, eL));
-            const double2 x3 = cmulc(buf[i0 + 3 * s * B], tw_at(tw, 3 * j, eL));
+            const double2 x1 = cmulc(buf[i0 + s * B], tw(j, eL));
+            const double2 x2 = cmulc(buf[i0 + 2 * s * B], tw(2 * j, eL));
+            const double2 x3 = cmulc(buf[i0 + 3 * s * B], tw(3 * j, eL));
             const double2 t0 = cadd(x0, x2), t1 = csub(x0, x2), t2 = cadd(x1, x3),
                           t3 = mul_i(csub(x1, x3));
             buf[i0] = cadd(t0, t2);
@@ -152,10 +183,10 @@ __device__ void lds_dit_inv(double2 *buf, int e, int B, const double2 *__restric
     }
     if (e & 1) {
         const int s = N >> 1;
-        for (int idx = threadIdx.x; idx < s * B; idx += FFT_T) {
+        for (int idx = threadIdx.x; idx < s * B; idx += blockDim.x) {
             const int j = idx / B, b = idx - j * B;
             const double2 y = buf[j * B + b];
-            const double2 z = cmulc(buf[(j + s) * B + b], tw_at(tw, j, e));
+            const double2 z = cmulc(buf[(j + s) * B + b], tw(j, e));
             buf[j * B + b] = cadd(y, z);
             buf[(j + s) * B + b] = csub(y, z);
         }
@@ -175,25 +206,27 @@ __global__ __launch_bounds__(FFT_T) void fft_twiddles(double2 *__restrict__ tw) 
 // Rows 0 .. rows-1 of the half spectrum of a real u8 plane (src rows of srcW
 // bytes srcPitch apart, zero beyond srcW and below srcRows): row r's real DFT
 // of length Qn = 2M, columns 0 .. M, zeros in columns M+1 .. pitch-1.
-__global__ __launch_bounds__(FFT_T) void fft_rows_r2c(const uint8_t *__restrict__ src, int srcW,
+__global__ __launch_bounds__(ROW_T) void fft_rows_r2c(const uint8_t *__restrict__ src, int srcW,
                                                       int srcRows, size_t srcPitch, int eM,
                                                       double2 *__restrict__ spec, int pitch,
                                                       const double2 *__restrict__ tw) {
-    extern __shared__ double2 z[];
+    extern __shared__ double2 z[];  // [M] samples, then the quarter table of W_2M
     const int M = 1 << eM, r = blockIdx.x;
+    const TwLds tq{z + M, eM + 1};
+    load_quarter(z + M, eM + 1, tw);
     const uint8_t *row = src + (size_t)r * srcPitch;
-    for (int n = threadIdx.x; n < M; n += FFT_T) {
+    for (int n = threadIdx.x; n < M; n += ROW_T) {
         const int x = 2 * n;
         const double v0 = (r < srcRows && x < srcW) ? (double)row[x] : 0.0;
         const double v1 = (r < srcRows && x + 1 < srcW) ? (double)row[x + 1] : 0.0;
         z[n] = make_double2(v0, v1);
     }
     __syncthreads();
-    lds_dif(z, eM, 1, tw);
+    lds_dif(z, eM, 1, tq);
     // X[k] = E[k] + W_Qn^k O[k]: E = (Z[k] + conj Z[M-k]) / 2 the even
     // samples' DFT, O = -i (Z[k] - conj Z[M-k]) / 2 the odd samples'
     double2 *out = spec + (size_t)r * pitch;
-    for (int k = threadIdx.x; k < pitch; k += FFT_T) {
+    for (int k = threadIdx.x; k < pitch; k += ROW_T) {
         if (k > M) {
             out[k] = make_double2(0.0, 0.0);
             continue;
@@ -202,7 +235,7 @@ __global__ __launch_bounds__(FFT_T) void fft_rows_r2c(const uint8_t *__restrict_
         const double2 zm = conjd(z[fft_pos((M - k) & (M - 1), eM)]);
         const double2 E = scaled(cadd(zk, zm), 0.5);
         const double2 O = scaled(mul_mi(csub(zk, zm)), 0.5);
-        out[k] = cadd(E, cmul(tw_at(tw, k, eM + 1), O));
+        out[k] = cadd(E, cmul(tq(k, eM + 1), O));
     }
 }
 
@@ -228,9 +261,9 @@ __global__ __launch_bounds__(FFT_T) void fft_cols_pass1(double2 *__restrict__ sp
     }
     __syncthreads();
     if (INV)
-        lds_dit_inv(buf, eP1, FFT_TB, tw);
+        lds_dit_inv(buf, eP1, FFT_TB, TwGlobal{tw});
     else
-        lds_dif(buf, eP1, FFT_TB, tw);
+        lds_dif(buf, eP1, FFT_TB, TwGlobal{tw});
     for (int idx = threadIdx.x; idx < P1 * FFT_TB; idx += FFT_T) {
         const int p = idx / FFT_TB, c = idx - p * FFT_TB;
         const int row = p * P2 + n2;
@@ -258,14 +291,14 @@ __global__ __launch_bounds__(FFT_T) void fft_cols_pass2(const double2 *__restric
         buf[idx] = src[(r0 + q) * pitch + c0 + c];
     }
     __syncthreads();
-    lds_dif(buf, eP2, FFT_TB, tw);
+    lds_dif(buf, eP2, FFT_TB, TwGlobal{tw});
     if (CORR) {
         for (int idx = threadIdx.x; idx < P2 * FFT_TB; idx += FFT_T) {
             const int q = idx / FFT_TB, c = idx - q * FFT_TB;
             buf[idx] = cmulc(buf[idx], tspec[(r0 + q) * pitch + c0 + c]);
         }
         __syncthreads();
-        lds_dit_inv(buf, eP2, FFT_TB, tw);
+        lds_dit_inv(buf, eP2, FFT_TB, TwGlobal{tw});
     }
     for (int idx = threadIdx.x; idx < P2 * FFT_TB; idx += FFT_T) {
         const int q = idx / FFT_TB, c = idx - q * FFT_TB;
@@ -273,51 +306,52 @@ __global__ __launch_bounds__(FFT_T) void fft_cols_pass2(const double2 *__restric
     }
 }
 
-__device__ __forceinline__ long long sat_box_fft(const int64_t *S, int W, int x0, int y0, int x1,
-                                                 int y1) {
-    // 0 <= x0 < x1 <= W, 0 <= y0 < y1 guaranteed by the caller
-    const int64_t *rb = S + (size_t)(y1 - 1) * W;
-    long long D = rb[x1 - 1];
-    long long C = x0 > 0 ? rb[x0 - 1] : 0;
-    long long B = 0, A = 0;
-    if (y0 > 0) {
-        const int64_t *rt = S + (size_t)(y0 - 1) * W;
-        B = rt[x1 - 1];
-        A = x0 > 0 ? rt[x0 - 1] : 0;
-    }
-    return D - B - C + A;
-}
-
 // Output row y = blockIdx.x: the inverse real transform of spectrum row y
 // (E = (X[k] + conj X[M-k]) / 2, O = W_Qn^-k (X[k] - conj X[M-k]) / 2,
 // Z = E + i O, z = M x IDFT(Z)), SumIT = round(scale * sample), then SumI and
-// SumISq from the tables and the coefficient, as the generic route does.
-__global__ __launch_bounds__(FFT_T) void fft_rows_c2r_coef(const double2 *__restrict__ spec,
+// SumISq by the four-corner rule on the tables and the coefficient, as the
+// generic route does.  The four corners are taken as differences of two
+// table rows staged once in LDS: cS[x] = S(x, y+hT-1) - S(x, y-1) (mod 2^32;
+// every window sum is below 2^32, so its difference of two cS is exact).
+__global__ __launch_bounds__(ROW_T) void fft_rows_c2r_coef(const double2 *__restrict__ spec,
                                                            int pitch, int eM, double scale,
                                                            CorrArgs a, int t,
                                                            const int64_t *__restrict__ S,
                                                            const int64_t *__restrict__ Q,
                                                            const double2 *__restrict__ tw) {
-    extern __shared__ double2 z[];
+    extern __shared__ double2 z[];  // [M] samples, [M/2] quarter table, then cS, cQ [W] each
     const int M = 1 << eM, y = blockIdx.x;
+    const TwLds tq{z + M, eM + 1};
+    uint32_t *cS = (uint32_t *)(z + M + M / 2), *cQ = cS + a.W;
+    load_quarter(z + M, eM + 1, tw);
+    {
+        const int64_t *sb = S + (size_t)(y + a.hT - 1) * a.W, *qb = Q + (size_t)(y + a.hT - 1) * a.W;
+        const int64_t *st = S + (size_t)(y > 0 ? y - 1 : 0) * a.W;
+        const int64_t *qt = Q + (size_t)(y > 0 ? y - 1 : 0) * a.W;
+        for (int x = threadIdx.x; x < a.W; x += ROW_T) {
+            cS[x] = (uint32_t)(sb[x] - (y > 0 ? st[x] : 0));
+            cQ[x] = (uint32_t)(qb[x] - (y > 0 ? qt[x] : 0));
+        }
+    }
+    __syncthreads();
     const double2 *in = spec + (size_t)y * pitch;
-    for (int k = threadIdx.x; k < M; k += FFT_T) {
+    for (int k = threadIdx.x; k < M; k += ROW_T) {
         const double2 xk = in[k], xm = conjd(in[M - k]);
         const double2 E = scaled(cadd(xk, xm), 0.5);
-        const double2 O = scaled(cmulc(csub(xk, xm), tw_at(tw, k, eM + 1)), 0.5);
+        const double2 O = scaled(cmulc(csub(xk, xm), tq(k, eM + 1)), 0.5);
         z[fft_pos(k, eM)] = cadd(E, mul_i(O));
     }
     __syncthreads();
-    lds_dit_inv(z, eM, 1, tw);
+    lds_dit_inv(z, eM, 1, tq);
     const TStat ts = a.stats[t];
     const long long K = (long long)a.wT * a.hT;
     const size_t o_row = (size_t)y * a.op;
-    for (int x = threadIdx.x; x < a.Wo; x += FFT_T) {
+    for (int x = threadIdx.x; x < a.Wo; x += ROW_T) {
         const double2 zz = z[x >> 1];
         const double v = (x & 1) ? zz.y : zz.x;
         const long long sumIT = __double2ll_rn(v * scale);
-        const long long sumI = sat_box_fft(S, a.W, x, y, x + a.wT, y + a.hT);
-        const long long sumISq = sat_box_fft(Q, a.W, x, y, x + a.wT, y + a.hT);
+        const long long sumI = (long long)(cS[x + a.wT - 1] - (x > 0 ? cS[x - 1] : 0u));
+        const long long sumISq = (long long)(cQ[x + a.wT - 1] - (x > 0 ? cQ[x - 1] : 0u));
         const long long num = K * sumIT - sumI * ts.sumT;
         const long long varI = K * sumISq - sumI * sumI;
         const size_t o = o_row + x;
@@ -397,14 +431,15 @@ hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q
     double2 *wspec = (double2 *)(base + 2 * spec);
     double2 *tw = (double2 *)(base + 3 * spec);
     const int M = 1 << g.eM, P = 1 << g.eP, P1 = 1 << g.eP1, P2 = 1 << g.eP2;
-    const size_t rowLds = (size_t)M * sizeof(double2);
+    const size_t rowLds = (size_t)(M + M / 2) * sizeof(double2);
+    const size_t c2rLds = rowLds + 2 * (size_t)a.W * sizeof(uint32_t);
     const size_t c1Lds = (size_t)P1 * FFT_TB * sizeof(double2);
     const size_t c2Lds = (size_t)P2 * FFT_TB * sizeof(double2);
     const dim3 blk(FFT_T);
 
     hipLaunchKernelGGL(fft_twiddles, dim3(TWN / FFT_T), blk, 0, st, tw);
     // the image's spectrum: rows of the view, then both column passes
-    hipLaunchKernelGGL(fft_rows_r2c, dim3(a.H), blk, rowLds, st, a.img, a.W, a.H, a.ip, g.eM, ispec,
+    hipLaunchKernelGGL(fft_rows_r2c, dim3(a.H), dim3(ROW_T), rowLds, st, a.img, a.W, a.H, a.ip, g.eM, ispec,
                        g.pitch, (const double2 *)tw);
     hipLaunchKernelGGL(fft_cols_pass1<false>, dim3(g.tiles, P2), blk, c1Lds, st, ispec, g.pitch,
                        g.eP1, g.eP2, a.H, P, (const double2 *)tw);
@@ -413,7 +448,7 @@ hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q
     const double scale = 1.0 / ((double)M * (double)P);
     for (int t = 0; t < a.nTpl; t++) {
         const uint8_t *T = a.tpl + (size_t)t * a.hT * a.wT;
-        hipLaunchKernelGGL(fft_rows_r2c, dim3(a.hT), blk, rowLds, st, T, a.wT, a.hT, (size_t)a.wT,
+        hipLaunchKernelGGL(fft_rows_r2c, dim3(a.hT), dim3(ROW_T), rowLds, st, T, a.wT, a.hT, (size_t)a.wT,
                            g.eM, tspec, g.pitch, (const double2 *)tw);
         hipLaunchKernelGGL(fft_cols_pass1<false>, dim3(g.tiles, P2), blk, c1Lds, st, tspec, g.pitch,
                            g.eP1, g.eP2, a.hT, P, (const double2 *)tw);
@@ -426,7 +461,7 @@ hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q
                            (const double2 *)tw);
         hipLaunchKernelGGL(fft_cols_pass1<true>, dim3(g.tiles, P2), blk, c1Lds, st, wspec, g.pitch,
                            g.eP1, g.eP2, P, a.Ho, (const double2 *)tw);
-        hipLaunchKernelGGL(fft_rows_c2r_coef, dim3(a.Ho), blk, rowLds, st, (const double2 *)wspec,
+        hipLaunchKernelGGL(fft_rows_c2r_coef, dim3(a.Ho), dim3(ROW_T), c2rLds, st, (const double2 *)wspec,
                            g.pitch, g.eM, scale, a, t, S, Q, (const double2 *)tw);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
