@@ -12,9 +12,10 @@ namespace ncc {
 
 namespace {
 
-constexpr int WG = 256;
+constexpr int WG = 1024;
 
-// One workgroup per template.
+// One workgroup per template (1024 lanes: a large template's loads spread
+// over many wavefronts instead of long per-lane loops).
 __global__ __launch_bounds__(WG) void tpl_prep(const uint8_t *__restrict__ tpl, int wT, int hT,
                                                uint32_t *__restrict__ rows,
                                                int8_t *__restrict__ mfma, int ksteps,
@@ -25,6 +26,7 @@ __global__ __launch_bounds__(WG) void tpl_prep(const uint8_t *__restrict__ tpl, 
 
     // exact sums
     unsigned long long s1 = 0, s2 = 0;
+#pragma unroll 4
     for (int i = tid; i < K; i += WG) {
         unsigned v = T[i];
         s1 += v;
@@ -56,6 +58,7 @@ __global__ __launch_bounds__(WG) void tpl_prep(const uint8_t *__restrict__ tpl, 
     // rows padded to whole dwords
     const int wt4 = (wT + 3) / 4;
     uint32_t *R = rows + (size_t)t * hT * wt4;
+#pragma unroll 2
     for (int i = tid; i < hT * wt4; i += WG) {
         const int j = i / wt4, k = i % wt4;
         uint32_t v = 0;
