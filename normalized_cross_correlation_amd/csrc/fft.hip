@@ -32,7 +32,8 @@ constexpr int TW_LOG = 14;
 constexpr int TWN = 1 << TW_LOG;  // twiddle table: exp(-2 pi i k / TWN), k < TWN
 constexpr int FFT_T = 256;        // threads per workgroup of the column passes
 constexpr int ROW_T = 1024;       // ... of the row transforms (one row per workgroup: enough
-                                  //   wavefronts per CU at up to 160 KB of LDS each)
+                                  //   wavefronts per CU at up to 96 KB of LDS each)
+constexpr int ROW_MAXX = 8;       // outputs per lane in the last row pass (8192 / ROW_T)
 constexpr int FFT_TB = 32;        // columns per workgroup in the column passes
 constexpr int FFT_MAX_LOG = 13;   // transform lengths up to 8192 per dimension
 
@@ -313,17 +314,37 @@ __global__ __launch_bounds__(FFT_T) void fft_cols_pass2(const double2 *__restric
 // generic route does.  The four corners are taken as differences of two
 // table rows staged once in LDS: cS[x] = S(x, y+hT-1) - S(x, y-1) (mod 2^32;
 // every window sum is below 2^32, so its difference of two cS is exact).
+// They reuse the samples' LDS once each lane holds its SumIT values (at most
+// ROW_MAXX of them: Wo <= 8192).
 __global__ __launch_bounds__(ROW_T) void fft_rows_c2r_coef(const double2 *__restrict__ spec,
                                                            int pitch, int eM, double scale,
                                                            CorrArgs a, int t,
                                                            const int64_t *__restrict__ S,
                                                            const int64_t *__restrict__ Q,
                                                            const double2 *__restrict__ tw) {
-    extern __shared__ double2 z[];  // [M] samples, [M/2] quarter table, then cS, cQ [W] each
+    extern __shared__ double2 z[];  // [M] samples (later cS, cQ [W] each), [M/2] quarter table
     const int M = 1 << eM, y = blockIdx.x;
     const TwLds tq{z + M, eM + 1};
-    uint32_t *cS = (uint32_t *)(z + M + M / 2), *cQ = cS + a.W;
     load_quarter(z + M, eM + 1, tw);
+    __syncthreads();  // the quarter table is read below
+    const double2 *in = spec + (size_t)y * pitch;
+    for (int k = threadIdx.x; k < M; k += ROW_T) {
+        const double2 xk = in[k], xm = conjd(in[M - k]);
+        const double2 E = scaled(cadd(xk, xm), 0.5);
+        const double2 O = scaled(cmulc(csub(xk, xm), tq(k, eM + 1)), 0.5);
+        z[fft_pos(k, eM)] = cadd(E, mul_i(O));
+    }
+    __syncthreads();
+    lds_dit_inv(z, eM, 1, tq);
+    long long sit[ROW_MAXX];
+#pragma unroll
+    for (int i = 0; i < ROW_MAXX; i++) {
+        const int x = threadIdx.x + i * ROW_T;
+        const double2 zz = z[(x < a.Wo ? x : 0) >> 1];
+        sit[i] = __double2ll_rn(((x & 1) ? zz.y : zz.x) * scale);
+    }
+    __syncthreads();  // the samples are read; their LDS takes cS, cQ
+    uint32_t *cS = (uint32_t *)z, *cQ = cS + a.W;
     {
         const int64_t *sb = S + (size_t)(y + a.hT - 1) * a.W, *qb = Q + (size_t)(y + a.hT - 1) * a.W;
         const int64_t *st = S + (size_t)(y > 0 ? y - 1 : 0) * a.W;
@@ -334,22 +355,14 @@ __global__ __launch_bounds__(ROW_T) void fft_rows_c2r_coef(const double2 *__rest
         }
     }
     __syncthreads();
-    const double2 *in = spec + (size_t)y * pitch;
-    for (int k = threadIdx.x; k < M; k += ROW_T) {
-        const double2 xk = in[k], xm = conjd(in[M - k]);
-        const double2 E = scaled(cadd(xk, xm), 0.5);
-        const double2 O = scaled(cmulc(csub(xk, xm), tq(k, eM + 1)), 0.5);
-        z[fft_pos(k, eM)] = cadd(E, mul_i(O));
-    }
-    __syncthreads();
-    lds_dit_inv(z, eM, 1, tq);
     const TStat ts = a.stats[t];
     const long long K = (long long)a.wT * a.hT;
     const size_t o_row = (size_t)y * a.op;
-    for (int x = threadIdx.x; x < a.Wo; x += ROW_T) {
-        const double2 zz = z[x >> 1];
-        const double v = (x & 1) ? zz.y : zz.x;
-        const long long sumIT = __double2ll_rn(v * scale);
+#pragma unroll
+    for (int i = 0; i < ROW_MAXX; i++) {
+        const int x = threadIdx.x + i * ROW_T;
+        if (x >= a.Wo) break;
+        const long long sumIT = sit[i];
         const long long sumI = (long long)(cS[x + a.wT - 1] - (x > 0 ? cS[x - 1] : 0u));
         const long long sumISq = (long long)(cQ[x + a.wT - 1] - (x > 0 ? cQ[x - 1] : 0u));
         const long long num = K * sumIT - sumI * ts.sumT;
@@ -432,7 +445,7 @@ hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q
     double2 *tw = (double2 *)(base + 3 * spec);
     const int M = 1 << g.eM, P = 1 << g.eP, P1 = 1 << g.eP1, P2 = 1 << g.eP2;
     const size_t rowLds = (size_t)(M + M / 2) * sizeof(double2);
-    const size_t c2rLds = rowLds + 2 * (size_t)a.W * sizeof(uint32_t);
+    const size_t c2rLds = rowLds;  // cS, cQ (8 W <= 16 M bytes) reuse the samples
     const size_t c1Lds = (size_t)P1 * FFT_TB * sizeof(double2);
     const size_t c2Lds = (size_t)P2 * FFT_TB * sizeof(double2);
     const dim3 blk(FFT_T);
