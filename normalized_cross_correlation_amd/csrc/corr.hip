@@ -188,16 +188,16 @@ __device__ __forceinline__ void stream_row(ST &st, const uint32_t (&d)[ST::WT4 +
 #pragma unroll
         for (int p = 0; p < POS; p++) g[p] = stream_coef(st, nI[p], sumISq[p], sumIT[p]);
         if (POS == 2 && st.pairs) {
-            __builtin_nontemporal_store((f2u){g[0], g[POS - 1]}, (f2u *)st.out + st.off);
+            __builtin_nontemporal_store((f2u){g[0], g[POS - 1]}, (f2u *)(st.out + st.off));
             if (ST::WSUM) {
                 if (st.wfirst) {
                     __builtin_nontemporal_store((i2u){-(int)nI[0], -(int)nI[POS - 1]},
-                                                (i2u *)st.s0 + st.off);
+                                                (i2u *)(st.s0 + st.off));
                     __builtin_nontemporal_store((i2u){(int)sumISq[0], (int)sumISq[POS - 1]},
-                                                (i2u *)st.s1 + st.off);
+                                                (i2u *)(st.s1 + st.off));
                 }
                 __builtin_nontemporal_store((i2u){(int)sumIT[0], (int)sumIT[POS - 1]},
-                                            (i2u *)st.s2 + st.off);
+                                            (i2u *)(st.s2 + st.off));
             }
         } else {
             // edge lanes: column p of this lane is min(first + p, Wo - 1)
