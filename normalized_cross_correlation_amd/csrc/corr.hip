@@ -555,9 +555,9 @@ hipError_t launch_stream_rs(const CorrArgs &a, int t, hipStream_t st) {
 }
 
 int device_cus() {
-    static int cus[64] = {0};
+    static int cus[NCC_MAX_DEVICES] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NCC_MAX_DEVICES) return 256;
     if (cus[dev] == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -661,13 +661,12 @@ hipError_t corr_generic_launch(const CorrArgs &a, int t, const int64_t *S, const
     generic_geometry(a.wT, a.hT, &pitch, &rowsT, &jb, &kb);
     size_t lds = (size_t)pitch * rowsT;
     if (lds > GEN_LDS) return hipErrorNotSupported;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)corr_generic,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, GEN_LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool attr_set[NCC_MAX_DEVICES] = {};
+    hipError_t e = set_once(attr_set, [] {
+        return hipFuncSetAttribute((const void *)corr_generic,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, GEN_LDS);
+    });
+    if (e != hipSuccess) return e;
     dim3 grid((a.Wo + GT - 1) / GT, (a.Ho + GT - 1) / GT);
     hipLaunchKernelGGL(corr_generic, grid, dim3(256), lds, st, a, t, S, Q, pitch, rowsT, jb, kb);
     return hipGetLastError();

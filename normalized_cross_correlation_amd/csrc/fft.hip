@@ -425,8 +425,8 @@ hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q
                            hipStream_t st) {
     FftGeom g;
     if (!fft_geometry(a.W, a.H, &g)) return hipErrorNotSupported;
-    static bool attr_set = false;
-    if (!attr_set) {
+    static bool attr_set[NCC_MAX_DEVICES] = {};
+    hipError_t ea = set_once(attr_set, [] {
         const size_t mx = 160 * 1024;
         hipError_t e;
         if ((e = set_lds((const void *)fft_rows_r2c, mx)) != hipSuccess) return e;
@@ -434,9 +434,9 @@ hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q
         if ((e = set_lds((const void *)fft_cols_pass1<false>, mx)) != hipSuccess) return e;
         if ((e = set_lds((const void *)fft_cols_pass1<true>, mx)) != hipSuccess) return e;
         if ((e = set_lds((const void *)fft_cols_pass2<false>, mx)) != hipSuccess) return e;
-        if ((e = set_lds((const void *)fft_cols_pass2<true>, mx)) != hipSuccess) return e;
-        attr_set = true;
-    }
+        return set_lds((const void *)fft_cols_pass2<true>, mx);
+    });
+    if (ea != hipSuccess) return ea;
     const size_t spec = ((size_t)g.pitch << g.eP) * sizeof(double2);
     char *base = (char *)work;
     double2 *ispec = (double2 *)base;

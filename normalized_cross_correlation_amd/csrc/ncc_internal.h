@@ -126,6 +126,23 @@ hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q
 bool corr_bank_supported(int wT, int hT, int nTpl);
 hipError_t corr_bank_launch(const CorrArgs &a, hipStream_t st);
 
+// ------------------------------------------------------ host utilities ---
+// Kernel attributes (the dynamic LDS limit above 64 KB) are set once per
+// device: set_once(flags, fn) runs fn on the current device unless it has
+// already succeeded there.  Running it twice from racing threads is harmless.
+constexpr int NCC_MAX_DEVICES = 64;
+template <class F>
+hipError_t set_once(bool (&flags)[NCC_MAX_DEVICES], F fn) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= NCC_MAX_DEVICES) return hipErrorInvalidDevice;
+    if (flags[dev]) return hipSuccess;
+    e = fn();
+    if (e == hipSuccess) flags[dev] = true;
+    return e;
+}
+
 // ---------------------------------------------------- device utilities ---
 #ifdef __HIP_DEVICE_COMPILE__
 #define NCC_DEV __device__ __forceinline__
