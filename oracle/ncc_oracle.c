@@ -20,7 +20,7 @@
  *             anchored at the window's top-left pixel, then calls
  *             CorrelationValue(SumI, SumISq, SumIT, SumT, cPixels, ...).
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - CorrelationValue's body is not on the pages.  The coefficient is the
  *     textbook Pearson / Lewis normalized cross-correlation in sum form:
  *       num  = K*SumIT - SumI*SumT
