@@ -131,14 +131,16 @@ int hip_status(hipError_t e) {
 }
 
 // Which correlation route to take; NCC_CORR_PATH selects one explicitly
-// ("generic", "fft", "single" for one template at a time, default "auto").
-enum class Route { Auto, Generic, Fft, Single };
+// ("generic", "fft", "single" for one template at a time, "dot4" for the
+// vector-unit streaming kernel, default "auto").
+enum class Route { Auto, Generic, Fft, Single, Dot4 };
 Route route_from_env() {
     const char *e = std::getenv("NCC_CORR_PATH");
     if (!e) return Route::Auto;
     if (!std::strcmp(e, "generic")) return Route::Generic;
     if (!std::strcmp(e, "fft")) return Route::Fft;
     if (!std::strcmp(e, "single")) return Route::Single;
+    if (!std::strcmp(e, "dot4")) return Route::Dot4;
     return Route::Auto;
 }
 
@@ -177,8 +179,11 @@ int correlate_request(const Request &r, hipStream_t st) {
     const int wT = r.wT, hT = r.hT, nTpl = r.nTpl;
     const Route route = route_from_env();
     const bool bank = route == Route::Auto && corr_bank_supported(wT, hT, nTpl);
-    const bool stream_ok =
-        (route == Route::Auto || route == Route::Single) && corr_stream_supported(wT, hT);
+    // single-template kernels: the matrix-core one, else the dot4 stream
+    const bool single_route = route == Route::Auto || route == Route::Single;
+    const bool toep_ok = single_route && corr_toeplitz_supported(wT, hT);
+    const bool stream_ok = toep_ok || ((single_route || route == Route::Dot4) &&
+                                       corr_stream_supported(wT, hT));
     const bool need_tables = !bank && !stream_ok;  // the generic and FFT routes
     if (need_tables && !corr_generic_supported(wT, hT)) return NCC_EUNSUPPORTED;
     const bool fft = need_tables && fft_chosen(route, r.w + wT - 1, r.h + hT - 1, r.w, r.h, wT,
@@ -217,7 +222,7 @@ int correlate_request(const Request &r, hipStream_t st) {
     // the streaming kernel derives everything from the caller's buffers
     if (!bank && stream_ok) {
         for (int t = 0; t < nTpl; t++) {
-            hipError_t e = corr_stream_launch(a, t, st);
+            hipError_t e = toep_ok ? corr_toeplitz_launch(a, t, st) : corr_stream_launch(a, t, st);
             if (e != hipSuccess) return hip_status(e);
         }
         return NCC_OK;

@@ -1,0 +1,423 @@
+// Single-template correlation on the int8 matrix cores, as a banded
+// Toeplitz product.
+//
+// What is computed is the per-window accumulation of The CUDA Handbook
+// ch. 15 "Image in shared memory" (SumI, SumISq, SumIT over a wT x hT
+// template, then the coefficient), with SumI and SumISq read off running
+// column sums of the image strip's row window sums (the four-corner rule of
+// section 15.8 on the strip's own summed-area table, horizontal difference
+// taken first).
+//
+// SumIT as a matrix product.  For template row j and the 16 positions
+// x0 + 16n + m (m = 0..15) of one 16-column block n, row j contributes
+//   sum_{u=0}^{31} T[j][u - m] * I[y + j][x0 + 16n + u]
+// (T[j][c] = 0 outside 0 <= c < wT): a 16 x 32 band matrix of the template
+// row times 32 image bytes.  With the 16 template rows stacked along k,
+//   C[m][n] = SumIT(x0 + 16n + m, y) = sum_k A[m][k] B[k][n],
+//   A[m][(j,u)] = T[j][u - m],  B[(j,u)][n] = I[y + j][x0 + 16n + u],
+// K = 16 rows x 32 = 512 k-slots, 8 steps of v_mfma_i32_16x16x64_i8 per 256
+// positions of one output row; half of A is structural zeros.  The
+// instruction multiplies signed bytes, so both sides move by 128 (T' = T^0x80
+// inside the band, 0 outside it; I' = I^0x80) and C = sum over the window of
+// I'T', from which
+//   num = K*SumIT - SumI*SumT = K*C + SumI*(128K - SumT) + 128K*SumT - 16384K^2
+// exactly (24-bit multiplies modulo 2^32; |num| < 2^31).
+//
+// Operand layout (16x16x64, as the bank kernel uses it): lane 16g + m of A
+// holds 16 k-slots of row m, lane 16g + n of B the same 16 k-slots of column
+// n, lane 16g + n of the result rows 4g .. 4g+3 of column n.  Step s, lane
+// group g covers template row j = s + 8(g >> 1), bytes u = 16(g & 1) .. +15.
+// So lane (g, n) holds, at output row y, image row y + s + 8(g >> 1) at
+// bytes 16(n + (g & 1)) .. +15 of its wavefront's columns: a ring of 8 image
+// rows per lane, one new 16-byte read per output row.  Its results are the
+// four adjacent positions x0 + 16n + 4g .. +3, whose window sums the same
+// lane forms from 5 dwords of the entering image row (sliding the window
+// across the 4 columns) and a ring of the last 16 rows' row window sums.
+//
+// A workgroup (4 wavefronts, 256 columns each) owns 1024 output columns and
+// RS output rows; image rows are staged 16 at a time into a 32-row LDS ring
+// (unsigned bytes) while the next batch is in flight in registers.
+#include "ncc_internal.h"
+
+namespace ncc {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef int i4u __attribute__((ext_vector_type(4), aligned(4)));
+
+constexpr int TZ_HT = 16;              // template rows
+constexpr int TZ_WAVES = 4;
+constexpr int TZ_NT = TZ_WAVES * 64;   // lanes per workgroup
+constexpr int TZ_NC = TZ_WAVES * 256;  // output columns per workgroup
+constexpr int TZ_CH = TZ_NC / 16 + 1;  // 16-byte chunks staged per row (tile + halo)
+constexpr int TZ_PITCH = TZ_CH * 4 + 4;  // dwords per LDS row
+constexpr int TZ_LOADS = (TZ_HT * TZ_CH + TZ_NT - 1) / TZ_NT;  // chunk loads per lane per batch
+// Row of each 16-row group before which the batch after next is staged:
+// rows y .. y + 16 + roff are read for output rows up to y + 1, so batch q is
+// no longer read once the group's row 7 is done.
+#ifndef TZ_PUT_ROW
+#define TZ_PUT_ROW 8
+#endif
+
+// Bytes x .. x+15 of row y (row y at img + y * ip) for images without
+// 16-byte aligned rows: five aligned dwords, byte-aligned.  Each dword
+// address is clamped to the dword holding the row's last byte, so every read
+// touches an image byte (an aligned dword never straddles a page).  Bytes
+// past the last row or column are then arbitrary: they feed only positions
+// past Ho or Wo, which are not stored.
+__device__ __forceinline__ uint4 tz_load16_any(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
+    const uint8_t *row = img + (size_t)min(y, H - 1) * ip;
+    const uintptr_t first = (uintptr_t)(row + min(x, W - 1));
+    const uintptr_t last = (uintptr_t)(row + W - 1) & ~(uintptr_t)3;
+    const uintptr_t base = first & ~(uintptr_t)3;
+    const uint32_t sh = (uint32_t)(first & 3);
+    uint32_t d[5];
+#pragma unroll
+    for (int k = 0; k < 5; k++) d[k] = *(const uint32_t *)min(base + 4 * k, last);
+    return make_uint4(align_bytes(d[1], d[0], sh), align_bytes(d[2], d[1], sh),
+                      align_bytes(d[3], d[2], sh), align_bytes(d[4], d[3], sh));
+}
+
+// Byte q (0..19) of the 5-dword little-endian sequence d.
+template <int Q>
+__device__ __forceinline__ uint32_t byte_at(const uint32_t (&d)[5]) {
+    return (d[Q >> 2] >> (8 * (Q & 3))) & 0xffu;
+}
+
+// Row window sums of I and I^2 at the four columns c0 .. c0+3 whose bytes
+// start at d[0] (byte 0 = column c0): the first window by dot4, then each
+// next one by adding the byte that enters and removing the one that leaves.
+template <int WT>
+__device__ __forceinline__ void row_sums4(const uint32_t (&d)[5], uint32_t (&h)[4], uint32_t (&q)[4]) {
+    constexpr int WT4 = (WT + 3) / 4;
+    uint32_t s = 0, s2 = 0;
+#pragma unroll
+    for (int k = 0; k < WT4; k++) {
+        const uint32_t v = (k == WT4 - 1) ? (d[k] & byte_mask(WT - 4 * k)) : d[k];
+        s = dot4u(v, 0x01010101u, s);
+        s2 = dot4u(v, v, s2);
+    }
+    h[0] = s;
+    q[0] = s2;
+#pragma unroll
+    for (int t = 0; t < 3; t++) {
+        uint32_t bo, bn;
+        // byte t leaves, byte t + WT enters
+        switch (t) {
+            case 0: bo = byte_at<0>(d); bn = byte_at<WT>(d); break;
+            case 1: bo = byte_at<1>(d); bn = byte_at<WT + 1>(d); break;
+            default: bo = byte_at<2>(d); bn = byte_at<WT + 2>(d); break;
+        }
+        const int dl = (int)bn - (int)bo, sm = (int)(bn + bo);
+        h[t + 1] = h[t] + (uint32_t)dl;
+        q[t + 1] = q[t] + (uint32_t)__mul24(dl, sm);
+    }
+}
+
+// Ring entry of one column's row window sums: I^2 sum in the high 20 bits,
+// I sum in the low 12 (wT <= 16: 16 * 255 < 2^12, 16 * 255^2 < 2^20).
+// The empty asm keeps the packed word opaque: otherwise the compiler keeps
+// both halves of every entry live and the ring no longer fits the registers.
+__device__ __forceinline__ uint32_t ring_pack(uint32_t h, uint32_t q) {
+    uint32_t p = (q << 12) | h;
+    __asm__ volatile("" : "+v"(p));
+    return p;
+}
+
+// Two workgroups (8 wavefronts) per CU: up to 256 registers per lane.
+#ifndef TZ_WPE
+#define TZ_WPE 2
+#endif
+template <int WT, int RS, int ALIGN, bool WSUM>
+__global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t, int ntx, int nty) {
+    static_assert(RS % 16 == 0 && RS >= 16, "strips of whole 16-row batches");
+    constexpr int NG = RS / 16;           // output-row groups of 16
+    constexpr int K = WT * TZ_HT;
+    __shared__ uint32_t buf[32][TZ_PITCH];  // image rows r at ring row r & 31
+    __shared__ uint32_t tE[TZ_HT][16];      // template row j at bytes 16 .. 16+wT-1 of 64, as T^0x80
+
+    const int tix = xcd_tile((int)blockIdx.x, ntx * nty);
+    if (tix < 0) return;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int g = l >> 4, n = l & 15;
+    const int X0 = (tix % ntx) * TZ_NC, y0 = (tix / ntx) * RS;
+    const int rowsOut = min(RS, a.Ho - y0);
+
+    // ---- staging of batch bt (image rows y0 + 16 bt .. +15) into registers
+    uint4 pre[TZ_LOADS];
+    auto fetch = [&](int bt) {
+#pragma unroll
+        for (int u = 0; u < TZ_LOADS; u++) {
+            const int i = tid + u * TZ_NT;
+            const int r = i / TZ_CH, c = i % TZ_CH;
+            const int y = y0 + 16 * bt + r, x = X0 + 16 * c;
+            if (ALIGN == 16) {
+                // W, ip % 16 == 0: clamped in-bounds addresses, no branch.  Bytes
+                // of rows past H or columns past W feed only positions past Ho
+                // or Wo, which are not stored, so what they hold is immaterial.
+                pre[u] = *(const uint4 *)(a.img + (size_t)min(y, a.H - 1) * a.ip + min(x, a.W - 16));
+            } else {
+                pre[u] = tz_load16_any(a.img, a.ip, a.W, a.H, x, y);
+            }
+        }
+    };
+    auto put = [&](int bt) {
+#pragma unroll
+        for (int u = 0; u < TZ_LOADS; u++) {
+            const int i = tid + u * TZ_NT;
+            if (i < TZ_HT * TZ_CH) {
+                const int r = i / TZ_CH, c = i % TZ_CH;
+                *(uint4 *)&buf[(16 * bt + r) & 31][4 * c] = pre[u];
+            }
+        }
+    };
+
+    fetch(0);
+    // template rows with a 16-byte zero margin on both sides, as signed bytes
+    const uint8_t *T = a.tpl + (size_t)t * TZ_HT * WT;
+    {  // 256 lanes: one dword each
+        const int j = tid / 16, dw = tid % 16;
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int c = 4 * dw + b - 16;
+            if (c >= 0 && c < WT) v |= (uint32_t)(T[j * WT + c] ^ 0x80u) << (8 * b);
+        }
+        tE[j][dw] = v;
+    }
+    put(0);
+    fetch(1);
+    __syncthreads();
+    put(1);
+
+    // ---- A operands: step s, lane (g, m = n): template row s + 8(g >> 1),
+    // bytes 16(g & 1) - m .. +15 of the row (zero outside it)
+    v4i atp[8];
+    {
+        const int st = 16 + 16 * (g & 1) - n;  // 1 .. 32
+        const int dw0 = st >> 2;
+        const uint32_t sh = (uint32_t)(st & 3);
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            const uint32_t *p = &tE[s + 8 * (g >> 1)][dw0];
+            const uint32_t e0 = p[0], e1 = p[1], e2 = p[2], e3 = p[3];
+            const uint32_t e4 = p[4];
+            atp[s] = (v4i){(int)align_bytes(e1, e0, sh), (int)align_bytes(e2, e1, sh),
+                           (int)align_bytes(e3, e2, sh), (int)align_bytes(e4, e3, sh)};
+        }
+    }
+    // template sums (every lane): T' = T - 128 sits at bytes 16 .. 31 of tE
+    int sT1 = 0, sT2 = 0;
+#pragma unroll
+    for (int j = 0; j < TZ_HT; j++)
+#pragma unroll
+        for (int k = 4; k < 8; k++) {
+            const uint32_t v = tE[j][k];
+            sT1 = __builtin_amdgcn_sdot4((int)v, 0x01010101, sT1, false);
+            sT2 = __builtin_amdgcn_sdot4((int)v, (int)v, sT2, false);
+        }
+    // SumT = sum T' + 128K; varT = K * sum T'^2 - (sum T')^2 (shift-invariant;
+    // <= K^2 * 127.5^2 < 2^31)
+    const int sumT = sT1 + 128 * K;
+    const float varTf = (float)((unsigned)K * (unsigned)sT2 - (unsigned)(sT1 * sT1));
+    const int ca = 128 * K - sumT;
+    const int cb = (int)((unsigned)(128 * K) * (unsigned)sumT - (unsigned)(16384 * K) * (unsigned)K);
+    __syncthreads();  // batches 0 and 1 staged
+
+    // ---- lane geometry
+    const int wcol = 256 * w;                      // wavefront's first column (rel. X0)
+    const int bch = wcol / 4 + 4 * (n + (g & 1));  // dword of the lane's B chunk
+    const int roff = 8 * (g >> 1);                 // B rows: y + s + roff
+    const int hdw = wcol / 4 + 4 * n + g;          // dword of the lane's window bytes
+    const int c0 = X0 + wcol + 16 * n + 4 * g;     // the lane's first position
+    const bool wfull = X0 + wcol >= a.xs && X0 + wcol + 256 <= a.Wo;  // wave-uniform
+
+    auto bload = [&](int r) -> v4i {  // image row r (rel. y0) of the lane's B chunk, as I^0x80
+        const uint4 v = *(const uint4 *)&buf[r & 31][bch];
+        return (v4i){(int)(v.x ^ 0x80808080u), (int)(v.y ^ 0x80808080u), (int)(v.z ^ 0x80808080u),
+                     (int)(v.w ^ 0x80808080u)};
+    };
+    auto hload = [&](int r, uint32_t (&d)[5]) {  // window bytes of image row r
+        const uint32_t *p = &buf[r & 31][hdw];
+#pragma unroll
+        for (int k = 0; k < 5; k++) d[k] = p[k];
+    };
+    auto hsum = [&](int r, uint32_t (&h)[4], uint32_t (&q)[4]) {
+        const uint32_t *p = &buf[r & 31][hdw];
+        const uint32_t d[5] = {p[0], p[1], p[2], p[3], p[4]};
+        row_sums4<WT>(d, h, q);
+    };
+
+    // B ring: slot r & 7 holds image row r + roff
+    v4i bring[8];
+#pragma unroll
+    for (int s = 0; s < 8; s++) bring[s] = bload(s + roff);
+    // row-sum ring: slot r & 15 holds image row r; window sums of output row 0
+    // start as the sums over image rows 0 .. 14
+    uint32_t ring[4][16];
+    uint32_t VI[4] = {0, 0, 0, 0}, VQ[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 15; r++) {
+        uint32_t h[4], q[4];
+        hsum(r, h, q);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            ring[i][r] = ring_pack(h[i], q[i]);
+            VI[i] += h[i];
+            VQ[i] += q[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) ring[i][15] = 0;
+
+    // per-strip bases keep the per-lane offsets within 32 bits
+    const size_t plane = a.oplane;
+    float *outp = a.coef + (size_t)t * plane + (size_t)y0 * a.op;
+    int32_t *sp0 = WSUM ? a.sums + (size_t)y0 * a.op : nullptr;
+    int32_t *sp1 = WSUM ? sp0 + plane : nullptr;
+    int32_t *sp2 = WSUM ? a.sums + (size_t)(2 + t) * plane + (size_t)y0 * a.op : nullptr;
+    // Offsets are signed: a view may start left of its first output (xs > 0),
+    // so the first wavefront's row base lies before the row's first output.
+    // Within a strip they stay below RS * op < 2^31 (op < 2^24).
+    const int op = (int)a.op;
+    int orow = c0 - a.xs;          // the lane's first output of the next row
+
+    // Software pipeline: iteration y reads from LDS what row y + 1 needs,
+    // issues the matrix-core chain of row y + 1 and finishes row y (window
+    // sums, epilogue, stores) while that chain runs.  Step s of row y reads B
+    // slot (y + s) & 7; step 7 of row y + 1 reads image row y + 8 + roff,
+    // read in iteration y - 1 and put into the slot row y's step 0 has read.
+    v4i accC = (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 8; s++) accC = __builtin_amdgcn_mfma_i32_16x16x64_i8(atp[s], bring[s], accC, 0, 0, 0);
+    uint32_t hd[5];  // window bytes of image row y + 15 (for row y)
+    hload(15, hd);
+    v4i nb = bload(8 + roff);  // step 7 of row 1
+
+#pragma unroll
+    for (int q = 0; q < NG; q++) {
+#pragma unroll
+        for (int yy = 0; yy < 16; yy++) {
+            const int y = 16 * q + yy;
+            // the batch after next is loaded during this group and staged in
+            // its middle, once every wavefront is past batch q
+            if (yy == 0 && q + 2 <= NG) fetch(q + 2);
+            if (yy == TZ_PUT_ROW && q + 2 <= NG) {
+                __syncthreads();
+                put(q + 2);
+                __syncthreads();
+            }
+            // reads for row y + 1
+            uint32_t hdN[5];
+            v4i nbN = nb;
+            if (y + 1 < RS) hload(y + 16, hdN);
+            if (y + 2 < RS) nbN = bload(y + 9 + roff);
+            v4i accN = (v4i){0, 0, 0, 0};
+            if (y + 1 < RS) {
+#pragma unroll
+                for (int s = 0; s < 7; s++)
+                    accN = __builtin_amdgcn_mfma_i32_16x16x64_i8(atp[s], bring[(yy + 1 + s) & 7], accN, 0, 0, 0);
+                accN = __builtin_amdgcn_mfma_i32_16x16x64_i8(atp[7], nb, accN, 0, 0, 0);
+                bring[yy & 7] = nb;
+            }
+            nb = nbN;
+            // window sums of row y: row y + 15 enters, row y - 1 leaves
+            uint32_t h[4], qq[4];
+            row_sums4<WT>(hd, h, qq);
+#pragma unroll
+            for (int k = 0; k < 5; k++) hd[k] = hdN[k];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t old = ring[i][(yy + 15) & 15];
+                VI[i] += h[i] - (old & 0xfffu);
+                VQ[i] += qq[i] - (old >> 12);
+                ring[i][(yy + 15) & 15] = ring_pack(h[i], qq[i]);
+            }
+            const v4i acc = accC;
+            accC = accN;
+
+            if (y < rowsOut) {  // wave-uniform
+                float gv[4];
+                int sI[4], sQ[4], sIT[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int sumI = (int)VI[i];
+                    const int num = __mul24(sumI, ca) + __mul24(K, acc[i]) + cb;
+                    const unsigned varI = __umul24((unsigned)K, VQ[i]) - (unsigned)__mul24(sumI, sumI);
+                    gv[i] = ncc_coef((float)num, (float)varI, varTf);
+                    sI[i] = sumI;
+                    sQ[i] = (int)VQ[i];
+                    sIT[i] = acc[i] + 128 * (sumI + sumT) - 16384 * K;
+                }
+                if (wfull) {
+                    __builtin_nontemporal_store((f4u){gv[0], gv[1], gv[2], gv[3]}, (f4u *)(outp + orow));
+                    if (WSUM) {
+                        if (t == 0) {
+                            __builtin_nontemporal_store((i4u){sI[0], sI[1], sI[2], sI[3]},
+                                                        (i4u *)(sp0 + orow));
+                            __builtin_nontemporal_store((i4u){sQ[0], sQ[1], sQ[2], sQ[3]},
+                                                        (i4u *)(sp1 + orow));
+                        }
+                        __builtin_nontemporal_store((i4u){sIT[0], sIT[1], sIT[2], sIT[3]},
+                                                    (i4u *)(sp2 + orow));
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int x = c0 + i;
+                        if (x >= a.xs && x < a.Wo) {
+                            outp[orow + i] = gv[i];
+                            if (WSUM) {
+                                if (t == 0) {
+                                    sp0[orow + i] = sI[i];
+                                    sp1[orow + i] = sQ[i];
+                                }
+                                sp2[orow + i] = sIT[i];
+                            }
+                        }
+                    }
+                }
+            }
+            orow += op;
+            // keep each iteration's loads and arithmetic inside it
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+template <int WT, int RS, bool WSUM>
+hipError_t launch_tz(const CorrArgs &a, int t, hipStream_t st) {
+    const int ntx = (a.Wo + TZ_NC - 1) / TZ_NC, nty = (a.Ho + RS - 1) / RS;
+    dim3 grid(xcd_grid(ntx * nty));
+    const uintptr_t al = (uintptr_t)a.img | (uintptr_t)a.ip;
+    if ((al & 15) == 0 && a.W % 16 == 0)
+        hipLaunchKernelGGL((corr_toeplitz<WT, RS, 16, WSUM>), grid, dim3(TZ_NT), 0, st, a, t, ntx, nty);
+    else
+        hipLaunchKernelGGL((corr_toeplitz<WT, RS, 1, WSUM>), grid, dim3(TZ_NT), 0, st, a, t, ntx, nty);
+    return hipGetLastError();
+}
+
+#ifndef TZ_RS
+#define TZ_RS 32
+#endif
+template <int WT>
+hipError_t launch_tz_w(const CorrArgs &a, int t, hipStream_t st) {
+    if (a.sums) return launch_tz<WT, TZ_RS, true>(a, t, st);
+    return launch_tz<WT, TZ_RS, false>(a, t, st);
+}
+
+}  // namespace
+
+bool corr_toeplitz_supported(int wT, int hT) { return hT == 16 && wT == 16; }
+
+hipError_t corr_toeplitz_launch(const CorrArgs &a, int t, hipStream_t st) {
+    if (a.hT != 16) return hipErrorNotSupported;
+    switch (a.wT) {
+        case 16: return launch_tz_w<16>(a, t, st);
+        default: return hipErrorNotSupported;
+    }
+}
+
+}  // namespace ncc

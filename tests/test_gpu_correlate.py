@@ -1,8 +1,9 @@
 """GPU parity of ncc_correlate against the oracle.
 
 Integer window sums must match bit for bit; float32 coefficients within
-1e-5 absolute.  Each route of the library (streaming single-template kernel,
-generic kernel on the full tables, int8 matrix-core bank kernel) is checked.
+1e-5 absolute.  Each route of the library (single-template kernels on the
+matrix cores and on the vector units, generic kernel on the full tables, int8
+matrix-core bank kernel) is checked.
 """
 import numpy as np
 import pytest
@@ -39,7 +40,7 @@ def test_small_config_exact_one_at_cut(oracle_mod):
     assert np.unravel_index(np.argmax(coef[0]), coef[0].shape) == (y, x)
 
 
-@pytest.mark.parametrize("rname", [None, "generic"])
+@pytest.mark.parametrize("rname", [None, "dot4", "generic"])
 @pytest.mark.parametrize("H,W,hT,wT,kind,seed", [
     (16, 16, 16, 16, "uniform", 1),     # one output
     (40, 300, 16, 16, "smooth", 2),     # ragged columns past one workgroup
@@ -63,13 +64,13 @@ def test_single_template_routes(oracle_mod, rname, H, W, hT, wT, kind, seed):
     (96, 256, 16, 16, 54),    # 81 rows
 ])
 def test_stream_strip_heights(oracle_mod, monkeypatch, rs, H, W, hT, wT, seed):
-    """The streaming kernel at each strip height (chosen per launch from the
-    output size; fixed here)."""
+    """The vector-unit streaming kernel at each strip height (chosen per
+    launch from the output size; fixed here)."""
     d = need_gpu()
     monkeypatch.setenv("NCC_STREAM_RS", rs)
     announce("correlate stream rs=%s %dx%d tpl %dx%d" % (rs, H, W, hT, wT))
     c = synth.random_case(seed, H, W, hT, wT, nTpl=1, kind="smooth")
-    _compare(oracle_mod, c["img"], c["tpl"], d)
+    _compare(oracle_mod, c["img"], c["tpl"], d, route_name="dot4")
 
 
 @pytest.mark.parametrize("H,W,hT,wT,seed", [

@@ -3,9 +3,10 @@ from a row-strided image, written to row-strided output) against the oracle.
 
 Sums bit for bit, coefficients within 1e-5 absolute; the padding between w
 and the output pitch is never written; a rectangle covering every position
-gives exactly ncc_correlate's output.  Each route is taken: the streaming
-kernel (on 16-byte aligned image rows it starts its view at the 16-byte
-boundary left of x0), the generic kernel on the rectangle's own tables
+gives exactly ncc_correlate's output.  Each route is taken: the
+single-template kernels on the matrix cores and on the vector units (on
+16-byte aligned image rows the view starts at the 16-byte boundary left of
+x0), the generic kernel on the rectangle's own tables
 (three-pass and single-pass builds) and the matrix-core bank.
 """
 import numpy as np
@@ -64,11 +65,13 @@ RECTS = [
 
 @pytest.mark.parametrize("x0,y0,w,h", RECTS)
 @pytest.mark.parametrize("layout", ["dense16", "pitched16", "pitched_odd"])
-def test_stream_rects(oracle_mod, layout, x0, y0, w, h):
-    """16 x 16 template: the streaming kernel, on 16-byte aligned rows (its
-    view starts left of x0) and on rows at odd addresses and pitch."""
+@pytest.mark.parametrize("kernel", [None, "dot4"])
+def test_stream_rects(oracle_mod, kernel, layout, x0, y0, w, h):
+    """16 x 16 template: the single-template kernels (matrix cores by
+    default, the vector-unit one forced), on 16-byte aligned rows (the view
+    starts left of x0) and on rows at odd addresses and pitch."""
     d = need_gpu()
-    announce("rect stream %s (%d,%d) %dx%d" % (layout, x0, y0, w, h))
+    announce("rect stream %s %s (%d,%d) %dx%d" % (kernel, layout, x0, y0, w, h))
     c = synth.random_case(200 + x0 + y0, 200, 320, 16, 16, nTpl=1, kind="smooth")
     img = c["img"]
     if layout == "dense16":
@@ -77,7 +80,8 @@ def test_stream_rects(oracle_mod, layout, x0, y0, w, h):
         iv = _strided_image(img, d, 32, 48)
     else:
         iv = _strided_image(img, d, 5, 2)
-    _check(oracle_mod, img, c["tpl"], d, x0, y0, w, h, out_pitch=w + 3, img_dev=iv)
+    with route(kernel):
+        _check(oracle_mod, img, c["tpl"], d, x0, y0, w, h, out_pitch=w + 3, img_dev=iv)
 
 
 @pytest.mark.parametrize("x0,y0,w,h", [(0, 0, 5, 5), (3, 9, 57, 41), (60, 2, 71, 80)])
