@@ -3,10 +3,12 @@
 //
 // What is computed is the per-window accumulation of The CUDA Handbook
 // ch. 15 "Image in shared memory" (SumI, SumISq, SumIT over a wT x hT
-// template, then the coefficient), with SumI and SumISq read off running
-// column sums of the image strip's row window sums (the four-corner rule of
-// section 15.8 on the strip's own summed-area table, horizontal difference
-// taken first).
+// template, then the coefficient).  SumIT and SumI are accumulated per
+// window, as that listing does, on the matrix cores; SumISq is read off
+// running column sums of the strip's row window sums of I^2 (the four-corner
+// rule of section 15.8 on the strip's own summed-area table of I^2, the
+// horizontal difference taken first).  Every sum is an exact integer, so the
+// route does not change a single output bit.
 //
 // SumIT as a matrix product.  For template row j and the 16 positions
 // x0 + 16n + m (m = 0..15) of one 16-column block n, row j contributes
@@ -30,13 +32,22 @@
 // So lane (g, n) holds, at output row y, image row y + s + 8(g >> 1) at
 // bytes 16(n + (g & 1)) .. +15 of its wavefront's columns: a ring of 8 image
 // rows per lane, one new 16-byte read per output row.  Its results are the
-// four adjacent positions x0 + 16n + 4g .. +3, whose window sums the same
-// lane forms from 5 dwords of the entering image row (sliding the window
-// across the 4 columns) and a ring of the last 16 rows' row window sums.
+// four adjacent positions x0 + 16n + 4g .. +3.
+//
+// Window sums.  SumI is the same product with an all-ones template, whose
+// band matrix does not depend on the template row: one constant A operand, a
+// second chain of 8 steps on the same B operands.  SumISq: the lane's row
+// sums of I^2 at its 4 positions (dot4 for the first, then the squares that
+// enter and leave as the window slides 1 byte), added down a ring of the
+// last 16 rows.
 //
 // A workgroup (4 wavefronts, 256 columns each) owns 1024 output columns and
-// RS output rows; image rows are staged 16 at a time into a 32-row LDS ring
-// (unsigned bytes) while the next batch is in flight in registers.
+// 32 output rows.  The strip's 48 image rows (rows + halo) are read once with
+// one round of 16-byte loads and staged in LDS (unsigned bytes); the loop
+// then runs without barriers.  Software pipeline: iteration y reads row y +
+// 1's LDS data and issues its chains, while finishing row y.  Before the
+// stores the results go through a lane permutation so that each store
+// instruction writes 1 KB of a row in lane order.
 #include "ncc_internal.h"
 
 namespace ncc {
@@ -53,13 +64,13 @@ constexpr int TZ_NT = TZ_WAVES * 64;   // lanes per workgroup
 constexpr int TZ_NC = TZ_WAVES * 256;  // output columns per workgroup
 constexpr int TZ_CH = TZ_NC / 16 + 1;  // 16-byte chunks staged per row (tile + halo)
 constexpr int TZ_PITCH = TZ_CH * 4 + 4;  // dwords per LDS row
-constexpr int TZ_LOADS = (TZ_HT * TZ_CH + TZ_NT - 1) / TZ_NT;  // chunk loads per lane per batch
-// Row of each 16-row group before which the batch after next is staged:
-// rows y .. y + 16 + roff are read for output rows up to y + 1, so batch q is
-// no longer read once the group's row 7 is done.
-#ifndef TZ_PUT_ROW
-#define TZ_PUT_ROW 8
-#endif
+constexpr int TZ_RS = 32;              // output rows per workgroup
+constexpr int TZ_ROWS = TZ_RS + 16;    // staged image rows (strip + halo, whole batches)
+constexpr int TZ_LOADS = (TZ_ROWS * TZ_CH + TZ_NT - 1) / TZ_NT;  // 16-byte loads per lane
+// Staged rows including the tail of the last round of loads (never read), so
+// that every load is stored without a branch: a guarded store lets the
+// compiler sink its load into the branch and wait for it there.
+constexpr int TZ_BUFROWS = (TZ_LOADS * TZ_NT + TZ_CH - 1) / TZ_CH;
 
 // Bytes x .. x+15 of row y (row y at img + y * ip) for images without
 // 16-byte aligned rows: five aligned dwords, byte-aligned.  Each dword
@@ -86,20 +97,19 @@ __device__ __forceinline__ uint32_t byte_at(const uint32_t (&d)[5]) {
     return (d[Q >> 2] >> (8 * (Q & 3))) & 0xffu;
 }
 
-// Row window sums of I and I^2 at the four columns c0 .. c0+3 whose bytes
-// start at d[0] (byte 0 = column c0): the first window by dot4, then each
-// next one by adding the byte that enters and removing the one that leaves.
+// Row window sums of I^2 at the four columns c0 .. c0+3 whose bytes start
+// at d[0] (byte 0 = column c0): the first window by dot4, then each next one
+// by adding the square that enters and removing the one that leaves
+// (b'^2 - b^2 = (b' - b)(b' + b)).
 template <int WT>
-__device__ __forceinline__ void row_sums4(const uint32_t (&d)[5], uint32_t (&h)[4], uint32_t (&q)[4]) {
+__device__ __forceinline__ void row_sq4(const uint32_t (&d)[5], uint32_t (&q)[4]) {
     constexpr int WT4 = (WT + 3) / 4;
-    uint32_t s = 0, s2 = 0;
+    uint32_t s2 = 0;
 #pragma unroll
     for (int k = 0; k < WT4; k++) {
         const uint32_t v = (k == WT4 - 1) ? (d[k] & byte_mask(WT - 4 * k)) : d[k];
-        s = dot4u(v, 0x01010101u, s);
         s2 = dot4u(v, v, s2);
     }
-    h[0] = s;
     q[0] = s2;
 #pragma unroll
     for (int t = 0; t < 3; t++) {
@@ -110,20 +120,20 @@ __device__ __forceinline__ void row_sums4(const uint32_t (&d)[5], uint32_t (&h)[
             case 1: bo = byte_at<1>(d); bn = byte_at<WT + 1>(d); break;
             default: bo = byte_at<2>(d); bn = byte_at<WT + 2>(d); break;
         }
-        const int dl = (int)bn - (int)bo, sm = (int)(bn + bo);
-        h[t + 1] = h[t] + (uint32_t)dl;
-        q[t + 1] = q[t] + (uint32_t)__mul24(dl, sm);
+        q[t + 1] = q[t] + (uint32_t)__mul24((int)bn - (int)bo, (int)(bn + bo));
     }
 }
 
-// Ring entry of one column's row window sums: I^2 sum in the high 20 bits,
-// I sum in the low 12 (wT <= 16: 16 * 255 < 2^12, 16 * 255^2 < 2^20).
-// The empty asm keeps the packed word opaque: otherwise the compiler keeps
-// both halves of every entry live and the ring no longer fits the registers.
-__device__ __forceinline__ uint32_t ring_pack(uint32_t h, uint32_t q) {
-    uint32_t p = (q << 12) | h;
-    __asm__ volatile("" : "+v"(p));
-    return p;
+// v[i] = the value v[i] of the lane whose byte address (lane * 4) is pidx.
+template <class V>
+__device__ __forceinline__ void to_lane_order(V (&v)[4], int pidx) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        int x;
+        __builtin_memcpy(&x, &v[i], 4);
+        x = __builtin_amdgcn_ds_bpermute(pidx, x);
+        __builtin_memcpy(&v[i], &x, 4);
+    }
 }
 
 // Two workgroups (8 wavefronts) per CU: up to 256 registers per lane.
@@ -132,10 +142,10 @@ __device__ __forceinline__ uint32_t ring_pack(uint32_t h, uint32_t q) {
 #endif
 template <int WT, int RS, int ALIGN, bool WSUM>
 __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t, int ntx, int nty) {
-    static_assert(RS % 16 == 0 && RS >= 16, "strips of whole 16-row batches");
+    static_assert(RS == TZ_RS, "the strip and its halo are staged whole");
     constexpr int NG = RS / 16;           // output-row groups of 16
     constexpr int K = WT * TZ_HT;
-    __shared__ uint32_t buf[32][TZ_PITCH];  // image rows r at ring row r & 31
+    __shared__ uint32_t buf[TZ_BUFROWS][TZ_PITCH];  // image rows y0 .. y0 + TZ_ROWS - 1 (+ tail)
     __shared__ uint32_t tE[TZ_HT][16];      // template row j at bytes 16 .. 16+wT-1 of 64, as T^0x80
 
     const int tix = xcd_tile((int)blockIdx.x, ntx * nty);
@@ -145,52 +155,51 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
     const int X0 = (tix % ntx) * TZ_NC, y0 = (tix / ntx) * RS;
     const int rowsOut = min(RS, a.Ho - y0);
 
-    // ---- staging of batch bt (image rows y0 + 16 bt .. +15) into registers
-    uint4 pre[TZ_LOADS];
-    auto fetch = [&](int bt) {
-#pragma unroll
-        for (int u = 0; u < TZ_LOADS; u++) {
-            const int i = tid + u * TZ_NT;
-            const int r = i / TZ_CH, c = i % TZ_CH;
-            const int y = y0 + 16 * bt + r, x = X0 + 16 * c;
-            if (ALIGN == 16) {
-                // W, ip % 16 == 0: clamped in-bounds addresses, no branch.  Bytes
-                // of rows past H or columns past W feed only positions past Ho
-                // or Wo, which are not stored, so what they hold is immaterial.
-                pre[u] = *(const uint4 *)(a.img + (size_t)min(y, a.H - 1) * a.ip + min(x, a.W - 16));
-            } else {
-                pre[u] = tz_load16_any(a.img, a.ip, a.W, a.H, x, y);
-            }
-        }
-    };
-    auto put = [&](int bt) {
-#pragma unroll
-        for (int u = 0; u < TZ_LOADS; u++) {
-            const int i = tid + u * TZ_NT;
-            if (i < TZ_HT * TZ_CH) {
-                const int r = i / TZ_CH, c = i % TZ_CH;
-                *(uint4 *)&buf[(16 * bt + r) & 31][4 * c] = pre[u];
-            }
-        }
-    };
-
-    fetch(0);
-    // template rows with a 16-byte zero margin on both sides, as signed bytes
+    // template bytes, loaded first from clamped indices (no branch)
     const uint8_t *T = a.tpl + (size_t)t * TZ_HT * WT;
-    {  // 256 lanes: one dword each
+    uint32_t tb[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        const int c = 4 * (tid % 16) + b - 16;
+        tb[b] = T[(tid / 16) * WT + min(max(c, 0), WT - 1)];
+    }
+    // ---- the strip's image rows, loaded all at once (one round of loads)
+    // and then staged in LDS; chunk i of the staged block is row i / TZ_CH,
+    // bytes 16 * (i % TZ_CH)
+    uint4 pre[TZ_LOADS];
+#pragma unroll
+    for (int u = 0; u < TZ_LOADS; u++) {
+        const int i = tid + u * TZ_NT;
+        const int r = i / TZ_CH, c = i % TZ_CH;
+        const int y = y0 + r, x = X0 + 16 * c;
+        if (ALIGN == 16) {
+            // W, ip % 16 == 0: clamped in-bounds addresses, no branch.  Bytes
+            // of rows past H or columns past W feed only positions past Ho
+            // or Wo, which are not stored, so what they hold is immaterial.
+            pre[u] = *(const uint4 *)(a.img + (size_t)min(y, a.H - 1) * a.ip + min(x, a.W - 16));
+        } else {
+            pre[u] = tz_load16_any(a.img, a.ip, a.W, a.H, x, y);
+        }
+    }
+    // template rows with a 16-byte zero margin on both sides, as signed
+    // bytes: lane (j, dw) builds dword dw of row j from its four bytes
+    {
         const int j = tid / 16, dw = tid % 16;
         uint32_t v = 0;
 #pragma unroll
         for (int b = 0; b < 4; b++) {
             const int c = 4 * dw + b - 16;
-            if (c >= 0 && c < WT) v |= (uint32_t)(T[j * WT + c] ^ 0x80u) << (8 * b);
+            v |= (c >= 0 && c < WT) ? (tb[b] ^ 0x80u) << (8 * b) : 0u;
         }
         tE[j][dw] = v;
     }
-    put(0);
-    fetch(1);
+#pragma unroll
+    for (int u = 0; u < TZ_LOADS; u++) {
+        const int i = tid + u * TZ_NT;
+        const int r = i / TZ_CH, c = i % TZ_CH;
+        *(uint4 *)&buf[r][4 * c] = pre[u];
+    }
     __syncthreads();
-    put(1);
 
     // ---- A operands: step s, lane (g, m = n): template row s + 8(g >> 1),
     // bytes 16(g & 1) - m .. +15 of the row (zero outside it)
@@ -224,48 +233,66 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
     const float varTf = (float)((unsigned)K * (unsigned)sT2 - (unsigned)(sT1 * sT1));
     const int ca = 128 * K - sumT;
     const int cb = (int)((unsigned)(128 * K) * (unsigned)sumT - (unsigned)(16384 * K) * (unsigned)K);
-    __syncthreads();  // batches 0 and 1 staged
 
     // ---- lane geometry
     const int wcol = 256 * w;                      // wavefront's first column (rel. X0)
     const int bch = wcol / 4 + 4 * (n + (g & 1));  // dword of the lane's B chunk
     const int roff = 8 * (g >> 1);                 // B rows: y + s + roff
     const int hdw = wcol / 4 + 4 * n + g;          // dword of the lane's window bytes
-    const int c0 = X0 + wcol + 16 * n + 4 * g;     // the lane's first position
+    // The lane's results are positions x0 + 16n + 4g .. +3 (x0 = X0 + wcol):
+    // consecutive lanes 64 bytes apart.  Before the stores, lane 4n + g takes
+    // lane 16g + n's four values through the LDS crossbar, so lane l holds
+    // positions x0 + 4l .. +3 and each store instruction writes 1 KB in lane
+    // order.
+    const int pidx = 4 * (16 * (l & 3) + (l >> 2));  // ds_bpermute byte address of the source lane
+    const int c0 = X0 + wcol + 4 * l;              // the lane's first position after that
     const bool wfull = X0 + wcol >= a.xs && X0 + wcol + 256 <= a.Wo;  // wave-uniform
 
     auto bload = [&](int r) -> v4i {  // image row r (rel. y0) of the lane's B chunk, as I^0x80
-        const uint4 v = *(const uint4 *)&buf[r & 31][bch];
+        const uint4 v = *(const uint4 *)&buf[r][bch];
         return (v4i){(int)(v.x ^ 0x80808080u), (int)(v.y ^ 0x80808080u), (int)(v.z ^ 0x80808080u),
                      (int)(v.w ^ 0x80808080u)};
     };
     auto hload = [&](int r, uint32_t (&d)[5]) {  // window bytes of image row r
-        const uint32_t *p = &buf[r & 31][hdw];
+        const uint32_t *p = &buf[r][hdw];
 #pragma unroll
         for (int k = 0; k < 5; k++) d[k] = p[k];
     };
-    auto hsum = [&](int r, uint32_t (&h)[4], uint32_t (&q)[4]) {
-        const uint32_t *p = &buf[r & 31][hdw];
-        const uint32_t d[5] = {p[0], p[1], p[2], p[3], p[4]};
-        row_sums4<WT>(d, h, q);
+    auto hsq = [&](int r, uint32_t (&q)[4]) {  // row sums of I^2 of image row r
+        uint32_t d[5];
+        hload(r, d);
+        row_sq4<WT>(d, q);
     };
 
     // B ring: slot r & 7 holds image row r + roff
     v4i bring[8];
 #pragma unroll
     for (int s = 0; s < 8; s++) bring[s] = bload(s + roff);
-    // row-sum ring: slot r & 15 holds image row r; window sums of output row 0
-    // start as the sums over image rows 0 .. 14
+    // SumI on the matrix cores too: the band matrix of an all-ones template
+    // is the same for every template row, so one A operand serves all 8
+    // steps (lane (g, m): byte i is 1 iff 0 <= 16(g & 1) + i - m < wT)
+    v4i aone;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int c = 16 * (g & 1) + 4 * k + b - n;
+            v |= (c >= 0 && c < WT) ? (1u << (8 * b)) : 0u;
+        }
+        aone[k] = (int)v;
+    }
+    // ring of row sums of I^2: slot r & 15 holds image row r; SumISq of
+    // output row 0 starts as the sum over image rows 0 .. 14
     uint32_t ring[4][16];
-    uint32_t VI[4] = {0, 0, 0, 0}, VQ[4] = {0, 0, 0, 0};
+    uint32_t VQ[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < 15; r++) {
-        uint32_t h[4], q[4];
-        hsum(r, h, q);
+        uint32_t q[4];
+        hsq(r, q);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            ring[i][r] = ring_pack(h[i], q[i]);
-            VI[i] += h[i];
+            ring[i][r] = q[i];
             VQ[i] += q[i];
         }
     }
@@ -289,9 +316,12 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
     // sums, epilogue, stores) while that chain runs.  Step s of row y reads B
     // slot (y + s) & 7; step 7 of row y + 1 reads image row y + 8 + roff,
     // read in iteration y - 1 and put into the slot row y's step 0 has read.
-    v4i accC = (v4i){0, 0, 0, 0};
+    v4i accC = (v4i){0, 0, 0, 0}, acoC = (v4i){0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < 8; s++) accC = __builtin_amdgcn_mfma_i32_16x16x64_i8(atp[s], bring[s], accC, 0, 0, 0);
+    for (int s = 0; s < 8; s++) {
+        accC = __builtin_amdgcn_mfma_i32_16x16x64_i8(atp[s], bring[s], accC, 0, 0, 0);
+        acoC = __builtin_amdgcn_mfma_i32_16x16x64_i8(aone, bring[s], acoC, 0, 0, 0);
+    }
     uint32_t hd[5];  // window bytes of image row y + 15 (for row y)
     hload(15, hd);
     v4i nb = bload(8 + roff);  // step 7 of row 1
@@ -301,56 +331,58 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
 #pragma unroll
         for (int yy = 0; yy < 16; yy++) {
             const int y = 16 * q + yy;
-            // the batch after next is loaded during this group and staged in
-            // its middle, once every wavefront is past batch q
-            if (yy == 0 && q + 2 <= NG) fetch(q + 2);
-            if (yy == TZ_PUT_ROW && q + 2 <= NG) {
-                __syncthreads();
-                put(q + 2);
-                __syncthreads();
-            }
             // reads for row y + 1
             uint32_t hdN[5];
             v4i nbN = nb;
             if (y + 1 < RS) hload(y + 16, hdN);
             if (y + 2 < RS) nbN = bload(y + 9 + roff);
-            v4i accN = (v4i){0, 0, 0, 0};
+            v4i accN = (v4i){0, 0, 0, 0}, acoN = (v4i){0, 0, 0, 0};
             if (y + 1 < RS) {
 #pragma unroll
-                for (int s = 0; s < 7; s++)
-                    accN = __builtin_amdgcn_mfma_i32_16x16x64_i8(atp[s], bring[(yy + 1 + s) & 7], accN, 0, 0, 0);
-                accN = __builtin_amdgcn_mfma_i32_16x16x64_i8(atp[7], nb, accN, 0, 0, 0);
+                for (int s = 0; s < 8; s++) {
+                    const v4i b = s < 7 ? bring[(yy + 1 + s) & 7] : nb;
+                    accN = __builtin_amdgcn_mfma_i32_16x16x64_i8(atp[s], b, accN, 0, 0, 0);
+                    acoN = __builtin_amdgcn_mfma_i32_16x16x64_i8(aone, b, acoN, 0, 0, 0);
+                }
                 bring[yy & 7] = nb;
             }
             nb = nbN;
-            // window sums of row y: row y + 15 enters, row y - 1 leaves
-            uint32_t h[4], qq[4];
-            row_sums4<WT>(hd, h, qq);
+            // SumISq of row y: row y + 15 enters, row y - 1 leaves
+            uint32_t qq[4];
+            row_sq4<WT>(hd, qq);
 #pragma unroll
             for (int k = 0; k < 5; k++) hd[k] = hdN[k];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const uint32_t old = ring[i][(yy + 15) & 15];
-                VI[i] += h[i] - (old & 0xfffu);
-                VQ[i] += qq[i] - (old >> 12);
-                ring[i][(yy + 15) & 15] = ring_pack(h[i], qq[i]);
+                VQ[i] += qq[i] - ring[i][(yy + 15) & 15];
+                ring[i][(yy + 15) & 15] = qq[i];
             }
-            const v4i acc = accC;
+            const v4i acc = accC, aco = acoC;
             accC = accN;
+            acoC = acoN;
 
-            if (y < rowsOut) {  // wave-uniform
-                float gv[4];
-                int sI[4], sQ[4], sIT[4];
+            // the coefficients are formed unconditionally (one basic block
+            // with the matrix-core chain, so the two interleave); only the
+            // stores depend on the row being an output row
+            float gv[4];
+            int sI[4], sQ[4], sIT[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int sumI = (int)VI[i];
-                    const int num = __mul24(sumI, ca) + __mul24(K, acc[i]) + cb;
-                    const unsigned varI = __umul24((unsigned)K, VQ[i]) - (unsigned)__mul24(sumI, sumI);
-                    gv[i] = ncc_coef((float)num, (float)varI, varTf);
-                    sI[i] = sumI;
-                    sQ[i] = (int)VQ[i];
-                    sIT[i] = acc[i] + 128 * (sumI + sumT) - 16384 * K;
-                }
+            for (int i = 0; i < 4; i++) {
+                const int sumI = aco[i] + 128 * K;  // the ones chain sums I^0x80
+                const int num = __mul24(sumI, ca) + __mul24(K, acc[i]) + cb;
+                const unsigned varI = __umul24((unsigned)K, VQ[i]) - (unsigned)__mul24(sumI, sumI);
+                gv[i] = ncc_coef((float)num, (float)varI, varTf);
+                sI[i] = sumI;
+                sQ[i] = (int)VQ[i];
+                sIT[i] = acc[i] + 128 * (sumI + sumT) - 16384 * K;
+            }
+            to_lane_order(gv, pidx);
+            if (WSUM) {
+                to_lane_order(sI, pidx);
+                to_lane_order(sQ, pidx);
+                to_lane_order(sIT, pidx);
+            }
+            if (y < rowsOut) {  // wave-uniform
                 if (wfull) {
                     __builtin_nontemporal_store((f4u){gv[0], gv[1], gv[2], gv[3]}, (f4u *)(outp + orow));
                     if (WSUM) {
@@ -399,9 +431,6 @@ hipError_t launch_tz(const CorrArgs &a, int t, hipStream_t st) {
     return hipGetLastError();
 }
 
-#ifndef TZ_RS
-#define TZ_RS 32
-#endif
 template <int WT>
 hipError_t launch_tz_w(const CorrArgs &a, int t, hipStream_t st) {
     if (a.sums) return launch_tz<WT, TZ_RS, true>(a, t, st);
@@ -410,11 +439,14 @@ hipError_t launch_tz_w(const CorrArgs &a, int t, hipStream_t st) {
 
 }  // namespace
 
-bool corr_toeplitz_supported(int wT, int hT) { return hT == 16 && wT == 16; }
+bool corr_toeplitz_supported(int wT, int hT) { return hT == 16 && wT >= 13 && wT <= 16; }
 
 hipError_t corr_toeplitz_launch(const CorrArgs &a, int t, hipStream_t st) {
     if (a.hT != 16) return hipErrorNotSupported;
     switch (a.wT) {
+        case 13: return launch_tz_w<13>(a, t, st);
+        case 14: return launch_tz_w<14>(a, t, st);
+        case 15: return launch_tz_w<15>(a, t, st);
         case 16: return launch_tz_w<16>(a, t, st);
         default: return hipErrorNotSupported;
     }

@@ -1,5 +1,6 @@
-"""GPU parity of the single-template matrix-core kernel (SumIT of a 16 x 16
-template as a banded Toeplitz product on the int8 matrix cores) against the
+"""GPU parity of the single-template matrix-core kernel (SumIT of a template
+16 rows high and 13 to 16 bytes wide as a banded Toeplitz product on the int8
+matrix cores, SumI as the same product with an all-ones template) against the
 oracle, and against the vector-unit streaming kernel.
 
 Sums bit for bit and coefficients within 1e-5 of the oracle.  Both kernels
@@ -50,6 +51,20 @@ def test_toeplitz_shapes(oracle_mod, H, W, kind, seed, want_sums):
     announce("toeplitz %dx%d %s sums=%s" % (H, W, kind, want_sums))
     c = synth.random_case(seed, H, W, 16, 16, nTpl=1, kind=kind)
     _check(oracle_mod, c["img"], c["tpl"], d, want_sums=want_sums)
+
+
+@pytest.mark.parametrize("wT", [13, 14, 15])
+@pytest.mark.parametrize("H,W,kind,seed", [
+    (60, 1104, "smooth", 71),    # two workgroups across, aligned rows
+    (50, 1037, "uniform", 72),   # rows not 16-byte aligned
+])
+def test_toeplitz_narrow_templates(oracle_mod, wT, H, W, kind, seed):
+    """16-row templates 13 to 15 bytes wide: the band and the all-ones
+    operands end early and the row sums of I^2 mask the last dword."""
+    d = need_gpu()
+    announce("toeplitz wT=%d %dx%d %s" % (wT, H, W, kind))
+    c = synth.random_case(seed + wT, H, W, 16, wT, nTpl=1, kind=kind)
+    _check(oracle_mod, c["img"], c["tpl"], d)
 
 
 def test_toeplitz_several_templates(oracle_mod):
