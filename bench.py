@@ -331,10 +331,10 @@ def main():
 
     sat_bytes = H * W * 17  # read u8 once, write two int64 tables once
     corr_ops = coeffs * hT * wT * 2  # u8 multiply-accumulates, 2 ops each
-    # the matrix-core kernel issues 8 v_mfma_i32_16x16x64_i8 (16*16*64*2 ops
-    # each) per 256 positions: 1024 int8 ops per coefficient, half of them on
-    # the band's structural zeros
-    corr_mfma_ops = coeffs * 1024
+    # the matrix-core kernel issues 16 v_mfma_i32_16x16x64_i8 (16*16*64*2 ops
+    # each) per 256 positions -- 8 for SumIT, 8 for SumI: 2048 int8 ops per
+    # coefficient, half of them on the bands' structural zeros
+    corr_mfma_ops = coeffs * 2048
     corr_bytes = H * W + coeffs * 4  # image read once, coefficients written once
     sat_rate = sat_bytes / (t_sat * 1e-3) / 1e9
     corr_rate = corr_ops / (t_corr * 1e-3) / 1e12
@@ -349,7 +349,7 @@ def main():
                           "frac_mfma": round(corr_mfma_ops / (t_corr * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
                           "useful_TOP/s": round(corr_rate, 2),
                           "frac_dot4_roof": round(corr_rate / DOT4_PEAK_TOPS, 4),
-                          "kernels": "corr_toeplitz<16,32> (int8 matrix cores)"},
+                          "kernels": "corr_toeplitz<16,32> (int8 matrix cores, 32-row strips)"},
     }
     if t_corr >= t_sat:
         roof = {"kernel": "corr_toeplitz<16,32> (ncc_correlate, one launch)", "bound": "hbm",

@@ -181,7 +181,10 @@ int correlate_request(const Request &r, hipStream_t st) {
     const bool bank = route == Route::Auto && corr_bank_supported(wT, hT, nTpl);
     // single-template kernels: the matrix-core one, else the dot4 stream
     const bool single_route = route == Route::Auto || route == Route::Single;
-    const bool toep_ok = single_route && corr_toeplitz_supported(wT, hT);
+    // (small launches, e.g. a local search, take the vector-unit kernel;
+    // NCC_CORR_PATH=single forces the matrix-core one where it applies)
+    const bool toep_ok = single_route && corr_toeplitz_supported(wT, hT) &&
+                         (route == Route::Single || corr_toeplitz_preferred(r.w, r.h));
     const bool stream_ok = toep_ok || ((single_route || route == Route::Dot4) &&
                                        corr_stream_supported(wT, hT));
     const bool need_tables = !bank && !stream_ok;  // the generic and FFT routes

@@ -111,6 +111,7 @@ hipError_t corr_stream_launch(const CorrArgs &a, int t, hipStream_t st);
 // Single template on the int8 matrix cores (SumIT as a banded Toeplitz
 // product; window sums from the strip's running column sums).
 bool corr_toeplitz_supported(int wT, int hT);
+bool corr_toeplitz_preferred(int Wo, int Ho);  // over the vector-unit kernel
 hipError_t corr_toeplitz_launch(const CorrArgs &a, int t, hipStream_t st);
 
 // Any shape: window sums from the full int64 tables S, Q.

@@ -50,6 +50,8 @@
 // instruction writes 1 KB of a row in lane order.
 #include "ncc_internal.h"
 
+#include <cstdlib>
+
 namespace ncc {
 
 namespace {
@@ -64,13 +66,23 @@ constexpr int TZ_NT = TZ_WAVES * 64;   // lanes per workgroup
 constexpr int TZ_NC = TZ_WAVES * 256;  // output columns per workgroup
 constexpr int TZ_CH = TZ_NC / 16 + 1;  // 16-byte chunks staged per row (tile + halo)
 constexpr int TZ_PITCH = TZ_CH * 4 + 4;  // dwords per LDS row
-constexpr int TZ_RS = 32;              // output rows per workgroup
-constexpr int TZ_ROWS = TZ_RS + 16;    // staged image rows (strip + halo, whole batches)
-constexpr int TZ_LOADS = (TZ_ROWS * TZ_CH + TZ_NT - 1) / TZ_NT;  // 16-byte loads per lane
-// Staged rows including the tail of the last round of loads (never read), so
-// that every load is stored without a branch: a guarded store lets the
-// compiler sink its load into the branch and wait for it there.
-constexpr int TZ_BUFROWS = (TZ_LOADS * TZ_NT + TZ_CH - 1) / TZ_CH;
+// SumISq keeps a ring of the last 16 rows' row sums of I^2 in registers
+// (TZ_RING 1), or recomputes the leaving row's sums from LDS (0; 126
+// registers, 4 wavefronts per SIMD at 16-row strips, measured no faster)
+#ifndef TZ_RING
+#define TZ_RING 1
+#endif
+// Strip of RS output rows: RS + 16 staged image rows (the strip and its
+// halo), read with LOADS 16-byte loads per lane; BUFROWS also holds the tail
+// of the last round of loads (never read), so that every load is stored
+// without a branch (a guarded store lets the compiler sink its load into the
+// branch and wait for it there).
+template <int RS>
+struct TzStrip {
+    static constexpr int ROWS = RS + 16;
+    static constexpr int LOADS = (ROWS * TZ_CH + TZ_NT - 1) / TZ_NT;
+    static constexpr int BUFROWS = (LOADS * TZ_NT + TZ_CH - 1) / TZ_CH;
+};
 
 // Bytes x .. x+15 of row y (row y at img + y * ip) for images without
 // 16-byte aligned rows: five aligned dwords, byte-aligned.  Each dword
@@ -138,15 +150,18 @@ __device__ __forceinline__ void to_lane_order(V (&v)[4], int pidx) {
 
 // Two workgroups (8 wavefronts) per CU: up to 256 registers per lane.
 #ifndef TZ_WPE
-#define TZ_WPE 2
+#define TZ_WPE (TZ_RING ? 2 : 4)
 #endif
 template <int WT, int RS, int ALIGN, bool WSUM>
 __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t, int ntx, int nty) {
-    static_assert(RS == TZ_RS, "the strip and its halo are staged whole");
+    static_assert(RS % 16 == 0, "strips of whole 16-row groups");
     constexpr int NG = RS / 16;           // output-row groups of 16
+    constexpr int TZ_LOADS = TzStrip<RS>::LOADS;
+    constexpr int TZ_BUFROWS = TzStrip<RS>::BUFROWS;
     constexpr int K = WT * TZ_HT;
     __shared__ uint32_t buf[TZ_BUFROWS][TZ_PITCH];  // image rows y0 .. y0 + TZ_ROWS - 1 (+ tail)
     __shared__ uint32_t tE[TZ_HT][16];      // template row j at bytes 16 .. 16+wT-1 of 64, as T^0x80
+    __shared__ int tsum[TZ_WAVES][2];       // per wavefront: sums of T' and T'^2
 
     const int tix = xcd_tile((int)blockIdx.x, ntx * nty);
     if (tix < 0) return;
@@ -192,6 +207,12 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
             v |= (c >= 0 && c < WT) ? (tb[b] ^ 0x80u) << (8 * b) : 0u;
         }
         tE[j][dw] = v;
+        const uint32_t p1 = wave_incl_scan_u32((uint32_t)__builtin_amdgcn_sdot4((int)v, 0x01010101, 0, false));
+        const uint32_t p2 = wave_incl_scan_u32((uint32_t)__builtin_amdgcn_sdot4((int)v, (int)v, 0, false));
+        if (l == 63) {
+            tsum[w][0] = (int)p1;
+            tsum[w][1] = (int)p2;
+        }
     }
 #pragma unroll
     for (int u = 0; u < TZ_LOADS; u++) {
@@ -217,16 +238,10 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
                            (int)align_bytes(e3, e2, sh), (int)align_bytes(e4, e3, sh)};
         }
     }
-    // template sums (every lane): T' = T - 128 sits at bytes 16 .. 31 of tE
-    int sT1 = 0, sT2 = 0;
-#pragma unroll
-    for (int j = 0; j < TZ_HT; j++)
-#pragma unroll
-        for (int k = 4; k < 8; k++) {
-            const uint32_t v = tE[j][k];
-            sT1 = __builtin_amdgcn_sdot4((int)v, 0x01010101, sT1, false);
-            sT2 = __builtin_amdgcn_sdot4((int)v, (int)v, sT2, false);
-        }
+    // template sums: each lane's tE dword (T' = T - 128, zeros around it),
+    // summed over the wavefront and then over the 4 wavefronts
+    const int sT1 = tsum[0][0] + tsum[1][0] + tsum[2][0] + tsum[3][0];
+    const int sT2 = tsum[0][1] + tsum[1][1] + tsum[2][1] + tsum[3][1];
     // SumT = sum T' + 128K; varT = K * sum T'^2 - (sum T')^2 (shift-invariant;
     // <= K^2 * 127.5^2 < 2^31)
     const int sumT = sT1 + 128 * K;
@@ -284,7 +299,9 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
     }
     // ring of row sums of I^2: slot r & 15 holds image row r; SumISq of
     // output row 0 starts as the sum over image rows 0 .. 14
+#if TZ_RING
     uint32_t ring[4][16];
+#endif
     uint32_t VQ[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < 15; r++) {
@@ -292,12 +309,16 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
         hsq(r, q);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
+#if TZ_RING
             ring[i][r] = q[i];
+#endif
             VQ[i] += q[i];
         }
     }
+#if TZ_RING
 #pragma unroll
     for (int i = 0; i < 4; i++) ring[i][15] = 0;
+#endif
 
     // per-strip bases keep the per-lane offsets within 32 bits
     const size_t plane = a.oplane;
@@ -324,6 +345,9 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
     }
     uint32_t hd[5];  // window bytes of image row y + 15 (for row y)
     hload(15, hd);
+#if !TZ_RING
+    uint32_t ho[5] = {0, 0, 0, 0, 0};  // ... and of row y - 1 (none for row 0)
+#endif
     v4i nb = bload(8 + roff);  // step 7 of row 1
 
 #pragma unroll
@@ -335,6 +359,10 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
             uint32_t hdN[5];
             v4i nbN = nb;
             if (y + 1 < RS) hload(y + 16, hdN);
+#if !TZ_RING
+            uint32_t hoN[5];
+            if (y + 1 < RS) hload(y, hoN);
+#endif
             if (y + 2 < RS) nbN = bload(y + 9 + roff);
             v4i accN = (v4i){0, 0, 0, 0}, acoN = (v4i){0, 0, 0, 0};
             if (y + 1 < RS) {
@@ -352,11 +380,25 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
             row_sq4<WT>(hd, qq);
 #pragma unroll
             for (int k = 0; k < 5; k++) hd[k] = hdN[k];
+#if TZ_RING
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 VQ[i] += qq[i] - ring[i][(yy + 15) & 15];
                 ring[i][(yy + 15) & 15] = qq[i];
             }
+#else
+            if (y > 0) {
+                uint32_t qo[4];
+                row_sq4<WT>(ho, qo);
+#pragma unroll
+                for (int i = 0; i < 4; i++) VQ[i] += qq[i] - qo[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++) VQ[i] += qq[i];
+            }
+#pragma unroll
+            for (int k = 0; k < 5; k++) ho[k] = hoN[k];
+#endif
             const v4i acc = accC, aco = acoC;
             accC = accN;
             acoC = acoN;
@@ -431,15 +473,48 @@ hipError_t launch_tz(const CorrArgs &a, int t, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Strip height: 32 rows halve the halo of 16-row strips, but a launch of
+// fewer than two 32-row workgroups per CU leaves CUs idle; then 16 rows
+// (measured: 28.7 vs 30.5 us at 4096 x 4096, 19.3 vs 16.5 us for a 2048 x
+// 2048 search rectangle).  NCC_TZ_STRIP = 16 or 32 fixes it instead.
+int tz_strip(const CorrArgs &a) {
+    if (const char *e = std::getenv("NCC_TZ_STRIP")) {
+        const int v = std::atoi(e);
+        if (v == 16 || v == 32) return v;
+    }
+    static int cus[NCC_MAX_DEVICES];
+    int dev = 0, n = 256;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < NCC_MAX_DEVICES) {
+        if (cus[dev] == 0) {
+            int v = 0;
+            cus[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                   hipSuccess && v > 0
+                           ? v
+                           : 256;
+        }
+        n = cus[dev];
+    }
+    const long long wgs32 = (long long)((a.Wo + TZ_NC - 1) / TZ_NC) * ((a.Ho + 31) / 32);
+    return wgs32 >= 2LL * n ? 32 : 16;
+}
+
 template <int WT>
 hipError_t launch_tz_w(const CorrArgs &a, int t, hipStream_t st) {
-    if (a.sums) return launch_tz<WT, TZ_RS, true>(a, t, st);
-    return launch_tz<WT, TZ_RS, false>(a, t, st);
+    const bool rs32 = tz_strip(a) == 32;
+    if (a.sums) return rs32 ? launch_tz<WT, 32, true>(a, t, st) : launch_tz<WT, 16, true>(a, t, st);
+    return rs32 ? launch_tz<WT, 32, false>(a, t, st) : launch_tz<WT, 16, false>(a, t, st);
 }
 
 }  // namespace
 
 bool corr_toeplitz_supported(int wT, int hT) { return hT == 16 && wT >= 13 && wT <= 16; }
+
+// A launch of fewer than 64 workgroups (1024 columns x 16 rows each) is
+// latency-bound, and there the vector-unit kernel's narrower workgroups are
+// faster (256 x 256 positions: 7.5 us against 10.6 us).
+bool corr_toeplitz_preferred(int Wo, int Ho) {
+    return (long long)((Wo + TZ_NC - 1) / TZ_NC) * ((Ho + 15) / 16) >= 64;
+}
 
 hipError_t corr_toeplitz_launch(const CorrArgs &a, int t, hipStream_t st) {
     if (a.hT != 16) return hipErrorNotSupported;

@@ -40,7 +40,7 @@ def test_small_config_exact_one_at_cut(oracle_mod):
     assert np.unravel_index(np.argmax(coef[0]), coef[0].shape) == (y, x)
 
 
-@pytest.mark.parametrize("rname", [None, "dot4", "generic"])
+@pytest.mark.parametrize("rname", [None, "single", "dot4", "generic"])
 @pytest.mark.parametrize("H,W,hT,wT,kind,seed", [
     (16, 16, 16, 16, "uniform", 1),     # one output
     (40, 300, 16, 16, "smooth", 2),     # ragged columns past one workgroup

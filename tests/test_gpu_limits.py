@@ -38,7 +38,8 @@ def test_sat_at_max_width(oracle_mod, monkeypatch, sat_path):
 
 
 @pytest.mark.parametrize("rname,n,hT,wT", [
-    (None, 1, 16, 16),        # streaming kernel
+    ("single", 1, 16, 16),    # single template on the matrix cores
+    ("dot4", 1, 16, 16),      # single template on the vector units
     ("generic", 1, 9, 11),    # the full tables
     (None, 3, 16, 16),        # matrix-core bank
 ])

@@ -65,11 +65,11 @@ RECTS = [
 
 @pytest.mark.parametrize("x0,y0,w,h", RECTS)
 @pytest.mark.parametrize("layout", ["dense16", "pitched16", "pitched_odd"])
-@pytest.mark.parametrize("kernel", [None, "dot4"])
+@pytest.mark.parametrize("kernel", ["single", "dot4"])
 def test_stream_rects(oracle_mod, kernel, layout, x0, y0, w, h):
-    """16 x 16 template: the single-template kernels (matrix cores by
-    default, the vector-unit one forced), on 16-byte aligned rows (the view
-    starts left of x0) and on rows at odd addresses and pitch."""
+    """16 x 16 template: both single-template kernels (matrix cores, vector
+    units), on 16-byte aligned rows (the view starts left of x0) and on rows
+    at odd addresses and pitch."""
     d = need_gpu()
     announce("rect stream %s %s (%d,%d) %dx%d" % (kernel, layout, x0, y0, w, h))
     c = synth.random_case(200 + x0 + y0, 200, 320, 16, 16, nTpl=1, kind="smooth")

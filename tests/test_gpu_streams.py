@@ -24,18 +24,23 @@ def _eager(ncc, img, tpl):
     return host(S), host(Q), host(coef), host(sums)
 
 
-@pytest.mark.parametrize("tshape,sat_path", [((16, 16, 1), "passes"), ((16, 16, 20), "passes"),
-                                             ((9, 11, 1), "passes"), ((16, 16, 1), "fused")])
-def test_graph_capture_replays(tshape, sat_path, monkeypatch):
-    """Table build + correlation captured once, replayed on changing images.
-    The single-pass table build keeps its call counters on the device, so its
-    replays need nothing from the host either."""
+@pytest.mark.parametrize("tshape,sat_path,corr_path", [
+    ((16, 16, 1), "passes", None), ((16, 16, 1), "passes", "single"),
+    ((16, 16, 20), "passes", None), ((9, 11, 1), "passes", None), ((16, 16, 1), "fused", None)])
+def test_graph_capture_replays(tshape, sat_path, corr_path, monkeypatch):
+    """Table build + correlation captured once, replayed on changing images
+    (the 16 x 16 single template on both of its kernels: vector units by
+    default at this size, matrix cores forced).  The single-pass table build
+    keeps its call counters on the device, so its replays need nothing from
+    the host either."""
     import torch
     import normalized_cross_correlation_amd as ncc
     d = need_gpu()
     monkeypatch.setenv("NCC_SAT_PATH", sat_path)
+    if corr_path:
+        monkeypatch.setenv("NCC_CORR_PATH", corr_path)
     hT, wT, n = tshape
-    announce("graph capture tpl %dx%d n=%d sat=%s" % (hT, wT, n, sat_path))
+    announce("graph capture tpl %dx%d n=%d sat=%s corr=%s" % (hT, wT, n, sat_path, corr_path))
     cases = [synth.random_case(60 + i, 173, 301, hT, wT, nTpl=n, kind="smooth") for i in range(3)]
     img = dev(cases[0]["img"], d)
     tpl = dev(cases[0]["tpl"], d)

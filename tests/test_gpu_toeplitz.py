@@ -35,7 +35,7 @@ def _check(oracle_mod, img, tpl, d, want_sums=True):
     return coef, co
 
 
-# H, W, image kind, seed: workgroups take 1024 output columns x 32 rows
+# H, W, image kind, seed: workgroups take 1024 output columns x 16 or 32 rows
 @pytest.mark.parametrize("H,W,kind,seed", [
     (16, 16, "uniform", 61),     # one output
     (47, 1040, "smooth", 62),    # two workgroups across (the second: 1 column)
@@ -46,9 +46,12 @@ def _check(oracle_mod, img, tpl, d, want_sums=True):
     (300, 70, "uniform", 67),    # tall and narrow
 ])
 @pytest.mark.parametrize("want_sums", [True, False])
-def test_toeplitz_shapes(oracle_mod, H, W, kind, seed, want_sums):
+@pytest.mark.parametrize("strip", ["16", "32"])
+def test_toeplitz_shapes(oracle_mod, monkeypatch, H, W, kind, seed, want_sums, strip):
+    """Both strip heights (chosen per launch from the grid size; fixed here)."""
     d = need_gpu()
-    announce("toeplitz %dx%d %s sums=%s" % (H, W, kind, want_sums))
+    monkeypatch.setenv("NCC_TZ_STRIP", strip)
+    announce("toeplitz %dx%d %s sums=%s strip=%s" % (H, W, kind, want_sums, strip))
     c = synth.random_case(seed, H, W, 16, 16, nTpl=1, kind=kind)
     _check(oracle_mod, c["img"], c["tpl"], d, want_sums=want_sums)
 
