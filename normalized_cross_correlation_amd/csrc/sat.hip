@@ -60,23 +60,40 @@ constexpr int ROWS_PER_WAVE = SAT_BH / 4;
 
 // Bytes x .. x+15 of row y.  VEC: W, ip and x multiples of 16, img 16-byte
 // aligned.
+// The zeroing is a mask, not a branch: a conditional assignment compiles to
+// a branch that waits for its load, which serialises the band's loads.
 template <bool VEC>
 __device__ __forceinline__ uint4 load16(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
     const uint8_t *row = img + (size_t)min(y, H - 1) * ip;
     uint4 v;
     if (VEC) {
         v = *(const uint4 *)(row + min(x, W - 16));
-        if (x >= W) v = make_uint4(0, 0, 0, 0);
+        const uint32_t m = (x < W && y < H) ? 0xffffffffu : 0u;
+        v.x &= m;
+        v.y &= m;
+        v.z &= m;
+        v.w &= m;
     } else {
-        uint32_t d[4] = {0, 0, 0, 0};
+        // five aligned dwords from addresses clamped to the dword holding the
+        // row's last byte (every read touches an image byte), byte-aligned;
+        // then bytes past W (and rows past H) are zeroed
+        const uint8_t *first = row + min(x, W - 1), *lastb = row + W - 1;
+        const uint32_t sh = (uint32_t)((uintptr_t)first & 3);
+        const uint32_t *base = (const uint32_t *)(first - sh);
+        const uint32_t *last = (const uint32_t *)(lastb - ((uintptr_t)lastb & 3));
+        uint32_t d[5];
 #pragma unroll
-        for (int k = 0; k < 16; k++) {
-            const uint32_t bk = row[min(x + k, W - 1)];
-            d[k >> 2] |= (x + k < W ? bk : 0u) << (8 * (k & 3));
+        for (int k = 0; k < 5; k++) d[k] = *(base + k <= last ? base + k : last);
+        const int valid = y < H ? min(max(W - x, 0), 16) : 0;  // bytes of the chunk inside
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const int nb = min(max(valid - 4 * k, 0), 4);
+            const uint32_t m = nb >= 4 ? 0xffffffffu : ((1u << (8 * nb)) - 1u);
+            o[k] = align_bytes(d[k + 1], d[k], sh) & m;
         }
-        v = make_uint4(d[0], d[1], d[2], d[3]);
+        v = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    if (y >= H) v = make_uint4(0, 0, 0, 0);
     return v;
 }
 

@@ -92,13 +92,13 @@ struct TzStrip {
 // past Ho or Wo, which are not stored.
 __device__ __forceinline__ uint4 tz_load16_any(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
     const uint8_t *row = img + (size_t)min(y, H - 1) * ip;
-    const uintptr_t first = (uintptr_t)(row + min(x, W - 1));
-    const uintptr_t last = (uintptr_t)(row + W - 1) & ~(uintptr_t)3;
-    const uintptr_t base = first & ~(uintptr_t)3;
-    const uint32_t sh = (uint32_t)(first & 3);
+    const uint8_t *first = row + min(x, W - 1), *lastb = row + W - 1;
+    const uint32_t sh = (uint32_t)((uintptr_t)first & 3);
+    const uint32_t *base = (const uint32_t *)(first - sh);
+    const uint32_t *last = (const uint32_t *)(lastb - ((uintptr_t)lastb & 3));
     uint32_t d[5];
 #pragma unroll
-    for (int k = 0; k < 5; k++) d[k] = *(const uint32_t *)min(base + 4 * k, last);
+    for (int k = 0; k < 5; k++) d[k] = *(base + k <= last ? base + k : last);
     return make_uint4(align_bytes(d[1], d[0], sh), align_bytes(d[2], d[1], sh),
                       align_bytes(d[3], d[2], sh), align_bytes(d[4], d[3], sh));
 }
