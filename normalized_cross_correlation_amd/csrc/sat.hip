@@ -257,7 +257,7 @@ __device__ __forceinline__ void top_load(TopChunk &ch, const uint32_t *__restric
     const int bb = min(bfirst + lane, nB - 1);
     uint64_t sp = 0;
     for (int s2 = 0; s2 < seg; s2++) sp += bs[(size_t)bb * nSeg + s2];
-    ch.sp = lane < n ? sp : 0u;
+    ch.sp = (lane < n && lane < TOP_CHUNK) ? sp : 0u;  // lanes past the chunk: next chunk's bands
 }
 
 __global__ __launch_bounds__(256) void sat_top(int W, SatWork wk) {

@@ -86,6 +86,19 @@ def test_generic_shapes(oracle_mod, H, W, hT, wT, seed):
 
 
 @pytest.mark.parametrize("H,W,hT,wT,seed", [
+    (4200, 1100, 5, 7, 41),    # over 128 table bands and two column segments
+    (8230, 2100, 16, 16, 42),
+])
+def test_generic_tall_and_wide(oracle_mod, H, W, hT, wT, seed):
+    """Window sums from tables of images taller than 4096 rows and wider than
+    1024 columns (several chunks of bands in the table build's top pass)."""
+    d = need_gpu()
+    announce("correlate generic tall %dx%d tpl %dx%d" % (H, W, hT, wT))
+    c = synth.random_case(seed, H, W, hT, wT, nTpl=1, kind="uniform")
+    _compare(oracle_mod, c["img"], c["tpl"], d, route_name="generic")
+
+
+@pytest.mark.parametrize("H,W,hT,wT,seed", [
     (40, 3000, 2, 2500, 31),   # wide: blocks of template dwords
     (2300, 40, 2200, 3, 32),   # tall: blocks of template rows
     (230, 420, 150, 200, 33),  # K = 30000, both

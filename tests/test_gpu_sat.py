@@ -30,6 +30,9 @@ SHAPES = [
     # widths that are not multiples of 4, several tiles
     (1, 1), (1, 300), (300, 1), (7, 5), (63, 255), (64, 256), (65, 257),
     (130, 515), (200, 1023), (129, 1030), (333, 777),
+    # more than 128 bands of 32 rows and more than one 1024-column segment:
+    # the top pass scans each quarter of the bands in several 32-band chunks
+    (4200, 1100), (8230, 1030), (4500, 2100),
 ]
 
 
