@@ -22,6 +22,7 @@ struct SatWork {
     int nStrips, nBands, nSeg;
     uint32_t *lrowl;    // [2][H][nStrips] row sum of the segment's strips left of each strip
     uint32_t *segtot;   // [2][H][nSeg]    row sum of each segment
+    uint32_t *segpre;   // [2][nSeg][H]    row sum of the segments left of each segment
     uint32_t *bandcol;  // [2][nBands][W]  band sum of the segment-local row running sums
     uint32_t *bandseg;  // [2][nBands][nSeg] band total of each segment
     uint64_t *top;      // [2][ceil(nBands/SAT_SUB)][W] table value on the row above

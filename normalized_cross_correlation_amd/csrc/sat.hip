@@ -11,7 +11,9 @@
 //      segment, i.e. the band's sum of the segment-local row running sums.
 //   2. sat_top: for every column, the exclusive scan of those band values down
 //      the bands (plus the segments to the left) is the table value on the
-//      row just above each band: S(x, y0 - 1), Q(x, y0 - 1).
+//      row just above each band: S(x, y0 - 1), Q(x, y0 - 1).  Beside these
+//      column blocks, row blocks form each row's running sum of the segment
+//      totals (the part of a row carry from the segments to the left).
 //   3. sat_downsweep: a workgroup owns a tile of SAT_SW columns x SAT_SUB
 //      bands and re-reads its bytes band by band (the next band's loads in
 //      flight while the current one is stored); the uint32 row running sums
@@ -34,20 +36,26 @@ constexpr int SAT_SPQ = SAT_QW / SAT_SW;   // strips per row-pass segment
 // the image afterwards (a select, not a branch), so the loads of all rows
 // issue back to back.
 
-// Pixels x, x+1 of row y (at img + y * ip) as the low 16 bits of a dword.
+// Pixels x, x+1 of row y (at img + y * ip) as the low 16 bits of a dword,
+// read from clamped in-bounds addresses (load2_raw) and then zeroed where
+// they lie outside the image (mask2).  Keeping the two apart lets a caller
+// issue a band's loads back to back and mask where it uses them.
 // VEC: W, ip and x even and img 2-byte aligned, so x < W implies x + 1 < W.
 template <bool VEC>
-__device__ __forceinline__ uint32_t load2(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
+__device__ __forceinline__ uint32_t load2_raw(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
     const uint8_t *row = img + (size_t)min(y, H - 1) * ip;
-    uint32_t v;
-    if (VEC) {
-        v = *(const uint16_t *)(row + min(x, W - 2));
-        v = x < W ? v : 0u;
-    } else {
-        const uint32_t b0 = row[min(x, W - 1)], b1 = row[min(x + 1, W - 1)];
-        v = (x < W ? b0 : 0u) | (x + 1 < W ? b1 << 8 : 0u);
-    }
-    return y < H ? v : 0u;
+    if (VEC) return *(const uint16_t *)(row + min(x, W - 2));
+    return (uint32_t)row[min(x, W - 1)] | ((uint32_t)row[min(x + 1, W - 1)] << 8);
+}
+
+__device__ __forceinline__ uint32_t mask2(uint32_t v, int W, int H, int x, int y) {
+    const uint32_t m = y >= H ? 0u : (x + 1 < W ? 0xffffu : (x < W ? 0xffu : 0u));
+    return v & m;
+}
+
+template <bool VEC>
+__device__ __forceinline__ uint32_t load2(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
+    return mask2(load2_raw<VEC>(img, ip, W, H, x, y), W, H, x, y);
 }
 
 // -------------------------------------------------------------- row pass --
@@ -256,12 +264,45 @@ __device__ __forceinline__ void top_load(TopChunk &ch, const uint32_t *__restric
     }
     const int bb = min(bfirst + lane, nB - 1);
     uint64_t sp = 0;
-    for (int s2 = 0; s2 < seg; s2++) sp += bs[(size_t)bb * nSeg + s2];
+    for (int s0 = 0; s0 < seg; s0 += 4) {  // 4 loads in flight together
+        uint32_t u4[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) u4[k] = bs[(size_t)bb * nSeg + min(s0 + k, seg - 1)];
+#pragma unroll
+        for (int k = 0; k < 4; k++) sp += s0 + k < seg ? u4[k] : 0u;
+    }
     ch.sp = (lane < n && lane < TOP_CHUNK) ? sp : 0u;  // lanes past the chunk: next chunk's bands
 }
 
-__global__ __launch_bounds__(256) void sat_top(int W, SatWork wk) {
+// Row sums of the segments left of each segment, for one row rr of [2][H]
+// (table, row): segpre[t][q][y] = sum of segtot[t][y][q'] over q' < q.
+// Four segments at a time, every load of a batch issued before the first
+// use; lanes take consecutive rows, so each store of a wavefront is 256
+// contiguous bytes.
+__device__ __forceinline__ void top_seg_prefix(const SatWork &wk, int H, int rr) {
+    const int nSeg = wk.nSeg, t = rr >= H, y = rr - t * H;
+    const uint32_t *__restrict__ st = wk.segtot + (size_t)rr * nSeg;
+    uint32_t *__restrict__ sp = wk.segpre + (size_t)t * nSeg * H + y;
+    uint32_t run = 0;
+    for (int q0 = 0; q0 < nSeg; q0 += 4) {
+        uint32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) v[k] = st[min(q0 + k, nSeg - 1)];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            if (q0 + k < nSeg) sp[(size_t)(q0 + k) * H] = run;
+            run += v[k];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void sat_top(int W, int H, SatWork wk) {
     const int colBlocks = (W + TOP_COLS - 1) / TOP_COLS;
+    if ((int)blockIdx.x >= 2 * colBlocks) {  // block-uniform: the row blocks
+        const int rr = ((int)blockIdx.x - 2 * colBlocks) * 256 + (int)threadIdx.x;
+        if (rr < 2 * H) top_seg_prefix(wk, H, rr);
+        return;
+    }
     const int t = blockIdx.x / colBlocks, cb = blockIdx.x % colBlocks;
     const int tid = threadIdx.x, c = tid & (TOP_COLS - 1), qtr = tid / TOP_COLS;
     const int x = cb * TOP_COLS + c, xc = min(x, W - 1);
@@ -314,28 +355,31 @@ __global__ __launch_bounds__(256) void sat_top(int W, SatWork wk) {
 // x = 128*s + 2l and x + 1, so each 16-byte store of a row lands next to its
 // neighbours' (1 KB per wavefront).
 
-// Bytes and left carries of one band for one wavefront: lane r < WAVE_ROWS
-// holds the left carry of row y0 + r (the segment-local carry plus the row
-// totals of the segments to the left).  Rows past the image read row H - 1;
-// their sums are never stored.
+// Bytes of one band for one wavefront, read from clamped addresses and
+// masked where they are used.
 template <bool VEC>
 struct BandIn {
     uint32_t px[WAVE_ROWS];
-    uint32_t lc1, lc2;
-    __device__ __forceinline__ void load(const uint8_t *img, size_t ip, int W, int H, const SatWork &wk,
-                                         int s, int x, int y0, int l) {
+    __device__ __forceinline__ void load(const uint8_t *img, size_t ip, int W, int H, int x, int y0) {
 #pragma unroll
-        for (int r = 0; r < WAVE_ROWS; r++) px[r] = load2<VEC>(img, ip, W, H, x, y0 + r);
-        const size_t r1 = (size_t)min(y0 + (l & (WAVE_ROWS - 1)), H - 1), r2 = (size_t)H + r1;
-        lc1 = wk.lrowl[r1 * wk.nStrips + s];
-        lc2 = wk.lrowl[r2 * wk.nStrips + s];
-        const int seg = s / SAT_SPQ;
-        for (int q2 = 0; q2 < seg; q2++) {
-            lc1 += wk.segtot[r1 * wk.nSeg + q2];
-            lc2 += wk.segtot[r2 * wk.nSeg + q2];
-        }
+        for (int r = 0; r < WAVE_ROWS; r++) px[r] = load2_raw<VEC>(img, ip, W, H, x, y0 + r);
     }
 };
+
+// Left carries of every row a wavefront writes in its tile, one per lane:
+// lane 32t + 8k + r holds, for table t, the row sum of all columns left of
+// the strip on row r of the wavefront's part of band k (the segment-local
+// carry plus the segments to the left).  Loaded and added once, before the
+// first band: within the band loop a use of a just-loaded value would wait
+// for every load issued before it, the next band's bytes included.
+static_assert(2 * SAT_SUB * WAVE_ROWS <= 64, "one left carry per lane");
+__device__ __forceinline__ uint32_t tile_left_carries(const SatWork &wk, int H, int s, int ytile, int w,
+                                                      int l) {
+    const int t = l >> 5, k = (l / WAVE_ROWS) % SAT_SUB, r = l % WAVE_ROWS;
+    const size_t y = (size_t)min(ytile + k * SAT_BH + w * WAVE_ROWS + r, H - 1);
+    const size_t seg = s / SAT_SPQ;
+    return wk.lrowl[((size_t)t * H + y) * wk.nStrips + s] + wk.segpre[((size_t)t * wk.nSeg + seg) * H + y];
+}
 
 template <bool VEC>
 __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__ img, int W, int H, size_t ip,
@@ -360,8 +404,9 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
         s2a = tp2[xa];
         s2b = tp2[xb];
     }
+    const uint32_t lcar = tile_left_carries(wk, H, s, ytile, w, l);
     BandIn<VEC> cur, nxt;
-    cur.load(img, ip, W, H, wk, s, x, ytile + w * WAVE_ROWS, l);
+    cur.load(img, ip, W, H, x, ytile + w * WAVE_ROWS);
 
     __shared__ uint64_t part[2][4][4][64];  // [band parity][wave][value][lane]
     typedef long long v2l __attribute__((ext_vector_type(2)));
@@ -375,15 +420,17 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
         // (left carry + wavefront exclusive scan + own pixels), and their
         // column totals over the wavefront's rows
         uint32_t R1a[WAVE_ROWS], R1b[WAVE_ROWS], R2a[WAVE_ROWS], R2b[WAVE_ROWS];
-        uint64_t c1a = 0, c1b = 0, c2a = 0, c2b = 0;
+        uint32_t c1a = 0, c1b = 0;  // 8 rows of R1 < 8 * 66051 * 255 < 2^32
+        uint64_t c2a = 0, c2b = 0;
 #pragma unroll
         for (int r = 0; r < WAVE_ROWS; r++) {
-            const uint32_t b0 = cur.px[r] & 0xffu, b1 = (cur.px[r] >> 8) & 0xffu;
+            const uint32_t pv = mask2(cur.px[r], W, H, x, y0 + r);
+            const uint32_t b0 = pv & 0xffu, b1 = pv >> 8;
             const uint32_t p1 = b0 + b1, p2 = b0 * b0 + b1 * b1;
             const uint32_t e1 = wave_incl_scan_u32(p1) - p1 +
-                                (uint32_t)__builtin_amdgcn_readlane((int)cur.lc1, r);
+                                (uint32_t)__builtin_amdgcn_readlane((int)lcar, WAVE_ROWS * k + r);
             const uint32_t e2 = wave_incl_scan_u32(p2) - p2 +
-                                (uint32_t)__builtin_amdgcn_readlane((int)cur.lc2, r);
+                                (uint32_t)__builtin_amdgcn_readlane((int)lcar, 32 + WAVE_ROWS * k + r);
             R1a[r] = e1 + b0;
             R1b[r] = e1 + p1;
             R2a[r] = e2 + b0 * b0;
@@ -394,7 +441,7 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
             c2b += R2b[r];
         }
         // the next band's inputs are in flight while this band is stored
-        if (k + 1 < SAT_SUB) nxt.load(img, ip, W, H, wk, s, x, y0 + SAT_BH, l);
+        if (k + 1 < SAT_SUB) nxt.load(img, ip, W, H, x, y0 + SAT_BH);
 
         const int pb = k & 1;
         part[pb][w][0][l] = c1a;
@@ -721,6 +768,7 @@ size_t sat_work_bytes(int W, int H) {
     auto add = [&](size_t n) { bytes += (n + 255) & ~(size_t)255; };
     add(2 * (size_t)H * nS * 4);  // lrowl
     add(2 * (size_t)H * nQ * 4);  // segtot
+    add(2 * (size_t)H * nQ * 4);  // segpre
     add(2 * nB * W * 4);          // bandcol
     add(2 * nB * nQ * 4);         // bandseg
     add(2 * ((nB + SAT_SUB - 1) / SAT_SUB) * W * 8);  // top
@@ -737,6 +785,7 @@ SatWork sat_work_carve(void *base, int W, int H) {
     auto take = [&](size_t n) { char *q = p; p += (n + 255) & ~(size_t)255; return (void *)q; };
     wk.lrowl = (uint32_t *)take(2 * (size_t)H * nS * 4);
     wk.segtot = (uint32_t *)take(2 * (size_t)H * nQ * 4);
+    wk.segpre = (uint32_t *)take(2 * (size_t)H * nQ * 4);
     wk.bandcol = (uint32_t *)take(2 * nB * W * 4);
     wk.bandseg = (uint32_t *)take(2 * nB * nQ * 4);
     wk.top = (uint64_t *)take(2 * ((nB + SAT_SUB - 1) / SAT_SUB) * W * 8);
@@ -788,7 +837,9 @@ hipError_t sat_build_launch(const uint8_t *img, int W, int H, size_t ip, int64_t
         hipLaunchKernelGGL(sat_rows<false>, rgrid, block, 0, st, img, W, H, ip, wk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sat_top, dim3(2 * ((W + TOP_COLS - 1) / TOP_COLS)), block, 0, st, W, wk);
+    const int rowBlocks = (2 * H + 255) / 256;
+    hipLaunchKernelGGL(sat_top, dim3(2 * ((W + TOP_COLS - 1) / TOP_COLS) + rowBlocks), block, 0, st, W,
+                       H, wk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid(xcd_grid(wk.nStrips * ((wk.nBands + SAT_SUB - 1) / SAT_SUB)));
