@@ -439,7 +439,8 @@ __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int
                                                     int rowsT, int jb, int kb) {
     extern __shared__ uint32_t tile[];  // rowsT x pitch bytes
     const int tid = threadIdx.x;
-    const int x0 = blockIdx.x * GT, y0 = blockIdx.y * GT;
+    const int ntx = (a.Wo + GT - 1) / GT;  // 1-D grid: any height
+    const int x0 = ((int)blockIdx.x % ntx) * GT, y0 = ((int)blockIdx.x / ntx) * GT;
     const int wt4 = (a.wT + 3) / 4;
     const int pw = pitch / 4;
     const int tx = tid & 15, ty = tid >> 4;
@@ -667,7 +668,7 @@ hipError_t corr_generic_launch(const CorrArgs &a, int t, const int64_t *S, const
                                    hipFuncAttributeMaxDynamicSharedMemorySize, GEN_LDS);
     });
     if (e != hipSuccess) return e;
-    dim3 grid((a.Wo + GT - 1) / GT, (a.Ho + GT - 1) / GT);
+    dim3 grid(((a.Wo + GT - 1) / GT) * ((a.Ho + GT - 1) / GT));
     hipLaunchKernelGGL(corr_generic, grid, dim3(256), lds, st, a, t, S, Q, pitch, rowsT, jb, kb);
     return hipGetLastError();
 }

@@ -117,7 +117,7 @@ __device__ __forceinline__ uint32_t oct_sum_u32(uint32_t x) {
 template <bool VEC>
 __global__ __launch_bounds__(256) void sat_rows(const uint8_t *__restrict__ img, int W, int H, size_t ip,
                                                 SatWork wk) {
-    const int q = blockIdx.x, b = blockIdx.y;
+    const int q = (int)blockIdx.x % wk.nSeg, b = (int)blockIdx.x / wk.nSeg;  // 1-D grid: any height
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int x = q * SAT_QW + 16 * l;
     const int y0 = b * SAT_BH + ROWS_PER_WAVE * w;
@@ -830,7 +830,7 @@ hipError_t sat_build_launch(const uint8_t *img, int W, int H, size_t ip, int64_t
     const bool dvec = (W % 2 == 0) && (ip % 2 == 0) && (((uintptr_t)img & 1) == 0) &&
                       (((uintptr_t)S & 15) == 0) && (((uintptr_t)Q & 15) == 0);
     dim3 block(256);
-    dim3 rgrid(wk.nSeg, wk.nBands);
+    dim3 rgrid(wk.nSeg * wk.nBands);
     if (rvec)
         hipLaunchKernelGGL(sat_rows<true>, rgrid, block, 0, st, img, W, H, ip, wk);
     else

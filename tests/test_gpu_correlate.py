@@ -88,6 +88,7 @@ def test_generic_shapes(oracle_mod, H, W, hT, wT, seed):
 @pytest.mark.parametrize("H,W,hT,wT,seed", [
     (4200, 1100, 5, 7, 41),    # over 128 table bands and two column segments
     (8230, 2100, 16, 16, 42),
+    (4300000, 2, 3, 1, 43),    # a one-dimensional signal: 67 188 output tiles down
 ])
 def test_generic_tall_and_wide(oracle_mod, H, W, hT, wT, seed):
     """Window sums from tables of images taller than 4096 rows and wider than
@@ -126,6 +127,7 @@ def test_medium_config(oracle_mod):
     (64, 16, 16, 47, 130, 24), (65, 16, 16, 40, 81, 25), (7, 8, 8, 33, 70, 26),
     (20, 16, 5, 45, 66, 27), (5, 4, 32, 30, 99, 28), (3, 1, 1, 20, 30, 29),
     (130, 16, 16, 30, 40, 30),
+    (3, 8, 8, 4200, 1100, 31),   # taller than 4096 rows, wider than 1024 columns
 ])
 def test_bank(oracle_mod, n, hT, wT, H, W, seed):
     d = need_gpu()

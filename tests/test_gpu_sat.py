@@ -33,6 +33,8 @@ SHAPES = [
     # more than 128 bands of 32 rows and more than one 1024-column segment:
     # the top pass scans each quarter of the bands in several 32-band chunks
     (4200, 1100), (8230, 1030), (4500, 2100),
+    # more row bands (68 750) and tiles than one grid dimension of 65 536
+    (2200000, 3),
 ]
 
 

@@ -70,6 +70,15 @@ def test_toeplitz_narrow_templates(oracle_mod, wT, H, W, kind, seed):
     _check(oracle_mod, c["img"], c["tpl"], d)
 
 
+def test_toeplitz_tall_and_wide(oracle_mod):
+    """An image taller than 4096 rows and wider than 1024 columns: 132 strips
+    of 32 rows, two workgroups across, a ragged last strip."""
+    d = need_gpu()
+    announce("toeplitz 4200x1100")
+    c = synth.random_case(70, 4200, 1100, 16, 16, nTpl=1, kind="smooth")
+    _check(oracle_mod, c["img"], c["tpl"], d)
+
+
 def test_toeplitz_several_templates(oracle_mod):
     """Three templates one at a time (one launch each): the window-sum planes
     written once, one SumIT plane per template."""
