@@ -132,8 +132,9 @@ int hip_status(hipError_t e) {
 
 // Which correlation route to take; NCC_CORR_PATH selects one explicitly
 // ("generic", "fft", "single" for one template at a time, "dot4" for the
-// vector-unit streaming kernel, default "auto").
-enum class Route { Auto, Generic, Fft, Single, Dot4 };
+// vector-unit streaming kernel, "tile" for the vector-unit tile kernel,
+// default "auto").
+enum class Route { Auto, Generic, Fft, Single, Dot4, Tile };
 Route route_from_env() {
     const char *e = std::getenv("NCC_CORR_PATH");
     if (!e) return Route::Auto;
@@ -141,6 +142,7 @@ Route route_from_env() {
     if (!std::strcmp(e, "fft")) return Route::Fft;
     if (!std::strcmp(e, "single")) return Route::Single;
     if (!std::strcmp(e, "dot4")) return Route::Dot4;
+    if (!std::strcmp(e, "tile")) return Route::Tile;
     return Route::Auto;
 }
 
@@ -187,7 +189,10 @@ int correlate_request(const Request &r, hipStream_t st) {
                          (route == Route::Single || corr_toeplitz_preferred(r.w, r.h));
     const bool stream_ok = toep_ok || ((single_route || route == Route::Dot4) &&
                                        corr_stream_supported(wT, hT));
-    const bool need_tables = !bank && !stream_ok;  // the generic and FFT routes
+    // the tile kernel: templates up to 32 x 64 that no kernel above takes
+    const bool tile_ok = !bank && !stream_ok && (route == Route::Auto || route == Route::Tile) &&
+                         corr_tile_supported(wT, hT);
+    const bool need_tables = !bank && !stream_ok && !tile_ok;  // the generic and FFT routes
     if (need_tables && !corr_generic_supported(wT, hT)) return NCC_EUNSUPPORTED;
     const bool fft = need_tables && fft_chosen(route, r.w + wT - 1, r.h + hT - 1, r.w, r.h, wT,
                                                hT, nTpl);
@@ -222,10 +227,12 @@ int correlate_request(const Request &r, hipStream_t st) {
     a.sums = r.sums;
     a.coef = r.coef;
 
-    // the streaming kernel derives everything from the caller's buffers
-    if (!bank && stream_ok) {
+    // the streaming and tile kernels derive everything from the caller's buffers
+    if (!bank && (stream_ok || tile_ok)) {
         for (int t = 0; t < nTpl; t++) {
-            hipError_t e = toep_ok ? corr_toeplitz_launch(a, t, st) : corr_stream_launch(a, t, st);
+            hipError_t e = tile_ok  ? corr_tile_launch(a, t, st)
+                           : toep_ok ? corr_toeplitz_launch(a, t, st)
+                                     : corr_stream_launch(a, t, st);
             if (e != hipSuccess) return hip_status(e);
         }
         return NCC_OK;

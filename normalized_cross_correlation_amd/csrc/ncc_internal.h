@@ -115,6 +115,11 @@ bool corr_toeplitz_supported(int wT, int hT);
 bool corr_toeplitz_preferred(int Wo, int Ho);  // over the vector-unit kernel
 hipError_t corr_toeplitz_launch(const CorrArgs &a, int t, hipStream_t st);
 
+// Templates up to 32 bytes wide and 64 rows high on the vector units, window
+// sums from the staged tile (no tables, no template preparation).
+bool corr_tile_supported(int wT, int hT);
+hipError_t corr_tile_launch(const CorrArgs &a, int t, hipStream_t st);
+
 // Any shape: window sums from the full int64 tables S, Q.
 bool corr_generic_supported(int wT, int hT);
 hipError_t corr_generic_launch(const CorrArgs &a, int t, const int64_t *S,

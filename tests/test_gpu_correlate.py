@@ -82,7 +82,7 @@ def test_generic_shapes(oracle_mod, H, W, hT, wT, seed):
     d = need_gpu()
     announce("correlate generic %dx%d tpl %dx%d" % (H, W, hT, wT))
     c = synth.random_case(seed, H, W, hT, wT, nTpl=1, kind="uniform")
-    _compare(oracle_mod, c["img"], c["tpl"], d)
+    _compare(oracle_mod, c["img"], c["tpl"], d, route_name="generic")
 
 
 @pytest.mark.parametrize("H,W,hT,wT,seed", [

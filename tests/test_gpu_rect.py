@@ -94,7 +94,8 @@ def test_generic_rects(oracle_mod, monkeypatch, sat_path, x0, y0, w, h):
     announce("rect generic sat=%s (%d,%d) %dx%d" % (sat_path, x0, y0, w, h))
     c = synth.random_case(300 + x0, 130, 145, 11, 9, nTpl=2, kind="uniform")
     iv = _strided_image(c["img"], d, 3, 9)
-    _check(oracle_mod, c["img"], c["tpl"], d, x0, y0, w, h, out_pitch=w + 1, img_dev=iv)
+    with route("generic"):
+        _check(oracle_mod, c["img"], c["tpl"], d, x0, y0, w, h, out_pitch=w + 1, img_dev=iv)
 
 
 def test_generic_route_forced_16x16(oracle_mod):

@@ -26,11 +26,13 @@ def _eager(ncc, img, tpl):
 
 @pytest.mark.parametrize("tshape,sat_path,corr_path", [
     ((16, 16, 1), "passes", None), ((16, 16, 1), "passes", "single"),
-    ((16, 16, 20), "passes", None), ((9, 11, 1), "passes", None), ((16, 16, 1), "fused", None)])
+    ((16, 16, 20), "passes", None), ((9, 11, 1), "passes", None), ((9, 11, 1), "passes", "generic"),
+    ((16, 16, 1), "fused", None)])
 def test_graph_capture_replays(tshape, sat_path, corr_path, monkeypatch):
     """Table build + correlation captured once, replayed on changing images
     (the 16 x 16 single template on both of its kernels: vector units by
-    default at this size, matrix cores forced).  The single-pass table build
+    default at this size, matrix cores forced; a 9 x 11 template on the tile
+    kernel by default and on the generic kernel, which reads the tables).  The single-pass table build
     keeps its call counters on the device, so its replays need nothing from
     the host either."""
     import torch
