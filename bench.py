@@ -208,7 +208,7 @@ def run_loop(args, L, sh, d):
         fns = [lambda: dst.copy_(src)]
     else:
         name = {"sat": "sat", "box": "sat", "corr": "headline", "rect": "headline",
-                "large": "headline", "bank": "bank"}[args.loop]
+                "large": "headline", "bank": "bank", "medium": "medium"}[args.loop]
         w = synth.make(name)
         img = torch.from_numpy(w["img"]).to(d)
         H, W = img.shape
@@ -267,7 +267,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="time only the headline step (used under the profiler)")
-    ap.add_argument("--loop", choices=["sat", "corr", "bank", "box", "rect", "large", "copy"],
+    ap.add_argument("--loop", choices=["sat", "corr", "bank", "box", "rect", "large", "medium", "copy"],
                     help="profiling aid: run one call type --steps times after --warmup and "
                          "exit without the JSON line (copy: a plain 256 MiB device copy, the "
                          "reference for scaling HBM byte counters)")
