@@ -9,24 +9,20 @@
 namespace ncc {
 
 // ---------------------------------------------------------------- tables ---
-// Table build tiling: the row pass takes bands of SAT_BH rows across
-// segments of SAT_QW columns; the downsweep takes tiles of SAT_SW columns x
-// SAT_SUB bands, a lane owning 2 adjacent columns and each of the 4
-// wavefronts SAT_BH / 4 rows of every band.
+// Table build tiling: tiles of SAT_SW columns x SAT_TR rows (strip s, tile
+// row g); the downsweep walks a tile in SAT_SUB bands of SAT_BH rows, a lane
+// owning 2 adjacent columns and each of the 4 wavefronts SAT_BH / 4 rows of
+// every band.
 constexpr int SAT_SW = 128;
 constexpr int SAT_BH = 32;
-constexpr int SAT_QW = 1024;
 constexpr int SAT_SUB = 4;
+constexpr int SAT_TR = SAT_BH * SAT_SUB;
 
 struct SatWork {
-    int nStrips, nBands, nSeg;
-    uint32_t *lrowl;    // [2][H][nStrips] row sum of the segment's strips left of each strip
-    uint32_t *segtot;   // [2][H][nSeg]    row sum of each segment
-    uint32_t *segpre;   // [2][nSeg][H]    row sum of the segments left of each segment
-    uint32_t *bandcol;  // [2][nBands][W]  band sum of the segment-local row running sums
-    uint32_t *bandseg;  // [2][nBands][nSeg] band total of each segment
-    uint64_t *top;      // [2][ceil(nBands/SAT_SUB)][W] table value on the row above
-                        //   each downsweep tile row
+    int nS, nG, nS4;   // strips, tile rows, strips rounded up to 4
+    uint32_t *colsum;  // [2][nG][nS*SAT_SW] each tile's column sums
+    uint32_t *btot;    // [2][nG][nS4]       each tile's total
+    uint32_t *lcar;    // [2][H][nS]         each row's sum over the columns left of each strip
 };
 
 // State of the single-pass build, kept per (device, stream) between calls:
@@ -167,6 +163,7 @@ constexpr int DPP_ROW_SHR1 = 0x111;
 constexpr int DPP_ROW_SHR2 = 0x112;
 constexpr int DPP_ROW_SHR4 = 0x114;
 constexpr int DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_ROR8 = 0x128;
 constexpr int DPP_ROW_BCAST15 = 0x142;
 constexpr int DPP_ROW_BCAST31 = 0x143;
 

@@ -3,34 +3,32 @@
 // Area Tables" -- table definition, width analysis (uint32 row running sums,
 // int64 table) and the separable build (a row scan, then a column scan).
 //
-// MI355X design: three passes with no waiting between workgroups.
-//   1. sat_rows: a workgroup reads one band of SAT_BH rows across a segment of
-//      SAT_QW columns once.  Per row it forms the strip sums and their running
-//      sum along the segment (the row carries of the third pass); per column
-//      it forms the band's column sums and their running sum along the
-//      segment, i.e. the band's sum of the segment-local row running sums.
-//   2. sat_top: for every column, the exclusive scan of those band values down
-//      the bands (plus the segments to the left) is the table value on the
-//      row just above each band: S(x, y0 - 1), Q(x, y0 - 1).  Beside these
-//      column blocks, row blocks form each row's running sum of the segment
-//      totals (the part of a row carry from the segments to the left).
-//   3. sat_downsweep: a workgroup owns a tile of SAT_SW columns x SAT_SUB
-//      bands and re-reads its bytes band by band (the next band's loads in
-//      flight while the current one is stored); the uint32 row running sums
-//      (left carry + wavefront DPP scan) stay in registers and are added down
-//      each column into int64 running sums that start from the pass-2 value
-//      above the tile.  S and Q are written once, lane l owning columns 2l
-//      and 2l+1 so one store instruction covers 1 KB of a table row.
+// MI355X design: two passes with no waiting between workgroups, over tiles
+// of SAT_SW columns x SAT_TR rows (strip s, tile row g).
+//   1. sat_tiles: tile workgroups read their tile once and write its column
+//      sums (colsum) and total (btot); row workgroups read 4 whole rows and
+//      write each row's exclusive running sum of strip sums (lcar: the row's
+//      sum left of each strip).
+//   2. sat_downsweep: a workgroup owns a tile.  Its prologue forms the table
+//      value on the row above the tile: the column sums of the tiles above
+//      (each wavefront a quarter of them, met in LDS), running along the
+//      strip, plus the totals of the tiles above and to the left.  It then
+//      re-reads its bytes band by band (the next band's loads in flight while
+//      the current one is stored); the uint32 row running sums (left carry +
+//      wavefront DPP scan) stay in registers and are added down each column
+//      into int64 running sums.  S and Q are written once, lane l owning
+//      columns 2l and 2l+1 so one store instruction covers 1 KB of a row.
 // The row running sums never go to HBM: the full-size traffic is two reads of
-// the image and one write of each table; the carries are a few MB.
+// the image and one write of each table; the tile sums are about 1 MB.
 #include "ncc_internal.h"
 
 namespace ncc {
 
 namespace {
 
-constexpr int WAVE_ROWS = SAT_BH / 4;      // downsweep rows per wavefront
-constexpr int SAT_SPQ = SAT_QW / SAT_SW;   // strips per row-pass segment
+constexpr int WAVE_ROWS = SAT_BH / 4;  // downsweep rows per wavefront
+constexpr int PRO_BATCH = 8;           // downsweep prologue: tile rows per wavefront per batch
+constexpr int PRO_BATCH_B = 2;         // ... block-total loads per thread per batch
 
 // Image loads take a clamped, in-bounds address and zero what lies outside
 // the image afterwards (a select, not a branch), so the loads of all rows
@@ -58,18 +56,20 @@ __device__ __forceinline__ uint32_t load2(const uint8_t *img, size_t ip, int W, 
     return mask2(load2_raw<VEC>(img, ip, W, H, x, y), W, H, x, y);
 }
 
-// -------------------------------------------------------------- row pass --
-// Workgroup (segment q, band b): wavefront w takes rows 8w .. 8w+7 of the
-// band and lane l the 16 columns q*SAT_QW + 16l .. +15 of each, so the 8
-// lanes l/8 = k cover strip k of the segment.  Bounds that keep the sums in
-// uint32: a segment row of 1024 squares and a band-segment of 32 x 1024
-// squares stay below 2^31; 8-row column sums of bytes fit 16 bits.
-constexpr int ROWS_PER_WAVE = SAT_BH / 4;
+// ------------------------------------------------------------- tile pass --
+// Sum over the 8 lanes 8g .. 8g+7, valid in lane 8g+7 (two quad butterflies,
+// then lanes 4..7 of each 8 add lanes 0..3).
+__device__ __forceinline__ uint32_t oct_sum_u32(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false);  // quad [1,0,3,2]
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false);  // quad [2,3,0,1]
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, DPP_ROW_SHR4, 0xf, 0xf, false);
+    return x;
+}
 
-// Bytes x .. x+15 of row y.  VEC: W, ip and x multiples of 16, img 16-byte
-// aligned.
-// The zeroing is a mask, not a branch: a conditional assignment compiles to
-// a branch that waits for its load, which serialises the band's loads.
+// Bytes x .. x+15 of row y, zero outside the image.  VEC: W, ip and x
+// multiples of 16, img 16-byte aligned.  The zeroing is a mask, not a
+// branch: a conditional assignment compiles to a branch that waits for its
+// load, which would serialise the tile's loads.
 template <bool VEC>
 __device__ __forceinline__ uint4 load16(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
     const uint8_t *row = img + (size_t)min(y, H - 1) * ip;
@@ -105,246 +105,135 @@ __device__ __forceinline__ uint4 load16(const uint8_t *img, size_t ip, int W, in
     return v;
 }
 
-// Sum over the 8 lanes 8g .. 8g+7, valid in lane 8g+7 (two quad butterflies,
-// then lanes 4..7 of each 8 add lanes 0..3).
-__device__ __forceinline__ uint32_t oct_sum_u32(uint32_t x) {
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false);  // quad [1,0,3,2]
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false);  // quad [2,3,0,1]
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, DPP_ROW_SHR4, 0xf, 0xf, false);
-    return x;
+// v_perm_b32: byte i of the result is byte sel_i of the 8 bytes hi:lo.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Two kinds of workgroup in one launch (blocks [0, nS*nG) are tiles, the
+// rest rows):
+//   tile (strip s, tile row g): thread (rg, cg) = (tid >> 3, tid & 7) holds
+//     rows 4rg .. 4rg+3 and columns 16cg .. 16cg+15 of the tile.  Writes the
+//     tile's column sums colsum[t][g][x] and its total btot[t][g][s].  Column
+//     sums of 4 rows come from 4x4 byte transposes (v_perm) and dot4 of each
+//     column's 4 bytes with ones and with itself; neighbouring row groups
+//     add through DPP and the remaining 16 meet in LDS.
+//   rows (rows 4b .. 4b+3, every column): thread tid holds columns
+//     16tid .. 16tid+15 of a 4096-column chunk; per row, strip sums (8 lanes
+//     each) and their exclusive running sum along the row: lcar[t][y][s], the
+//     row's sum over the columns left of strip s.
+// Every write covers whole 128-byte lines.  uint32 bounds: a tile column of
+// 128 squares, a tile total <= 128 * 128 * 255^2 < 2^31, a row prefix
+// <= W * 255^2 (the width bound).
+constexpr int ROW_CHUNK = 4096;  // columns of a row workgroup per step
+
+template <bool VEC>
+__device__ __forceinline__ void tile_sums(const uint8_t *__restrict__ img, int W, int H, size_t ip,
+                                          const SatWork &wk, int s, int g, uint32_t *lds) {
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int cg = tid & 7, rg = tid >> 3;
+    const int x = s * SAT_SW + 16 * cg, y0 = g * SAT_TR + 4 * rg;
+    uint4 px[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) px[r] = load16<VEC>(img, ip, W, H, x, y0 + r);
+    uint32_t(*red)[16][SAT_SW] = (uint32_t(*)[16][SAT_SW])lds;  // [table][row-group pair][column]
+    uint32_t *btw = lds + 2 * 16 * SAT_SW;                        // [wave] half-tile totals
+    // dword k of the 4 rows, transposed so that word c holds column 4k+c of
+    // rows 0..3; then lanes l and l^8 (row groups 2j, 2j+1) add
+    uint32_t ci[16], cq[16];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t d0 = ((const uint32_t *)&px[0])[k], d1 = ((const uint32_t *)&px[1])[k];
+        const uint32_t d2 = ((const uint32_t *)&px[2])[k], d3 = ((const uint32_t *)&px[3])[k];
+        const uint32_t e0 = perm(d1, d0, 0x06020400u), e1 = perm(d1, d0, 0x07030501u);
+        const uint32_t e2 = perm(d3, d2, 0x06020400u), e3 = perm(d3, d2, 0x07030501u);
+        const uint32_t tc[4] = {perm(e2, e0, 0x05040100u), perm(e3, e1, 0x05040100u), perm(e2, e0, 0x07060302u),
+                                perm(e3, e1, 0x07060302u)};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            ci[4 * k + c] = dot4u(tc[c], 0x01010101u, 0);
+            cq[4 * k + c] = dot4u(tc[c], tc[c], 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        ci[j] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ci[j], DPP_ROW_ROR8, 0xf, 0xf, false);
+        cq[j] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cq[j], DPP_ROW_ROR8, 0xf, 0xf, false);
+    }
+    if ((rg & 1) == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            *(uint4 *)&red[0][rg >> 1][16 * cg + 4 * k] = make_uint4(ci[4 * k], ci[4 * k + 1], ci[4 * k + 2], ci[4 * k + 3]);
+            *(uint4 *)&red[1][rg >> 1][16 * cg + 4 * k] = make_uint4(cq[4 * k], cq[4 * k + 1], cq[4 * k + 2], cq[4 * k + 3]);
+        }
+    }
+    __syncthreads();
+    // thread (table, column): the tile's column sum; the tile total per
+    // wavefront (two per table)
+    const int t = tid >> 7, c = tid & (SAT_SW - 1);
+    uint32_t cs = 0;
+#pragma unroll
+    for (int r = 0; r < 16; r++) cs += red[t][r][c];
+    wk.colsum[((size_t)t * wk.nG + g) * ((size_t)wk.nS * SAT_SW) + (size_t)s * SAT_SW + c] = cs;
+    const uint32_t tot = wave_sum_u32(cs);
+    if (l == 0) btw[w] = tot;
+    __syncthreads();
+    if (tid < 2) wk.btot[((size_t)tid * wk.nG + g) * wk.nS4 + s] = btw[2 * tid] + btw[2 * tid + 1];
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void sat_rows(const uint8_t *__restrict__ img, int W, int H, size_t ip,
-                                                SatWork wk) {
-    const int q = (int)blockIdx.x % wk.nSeg, b = (int)blockIdx.x / wk.nSeg;  // 1-D grid: any height
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int x = q * SAT_QW + 16 * l;
-    const int y0 = b * SAT_BH + ROWS_PER_WAVE * w;
-    uint4 px[ROWS_PER_WAVE];
+__device__ __forceinline__ void row_prefixes(const uint8_t *__restrict__ img, int W, int H, size_t ip,
+                                             const SatWork &wk, int b, uint32_t *lds) {
+    const int tid = threadIdx.x;
+    const int y0 = 4 * b;
+    uint32_t(*ss)[4][32] = (uint32_t(*)[4][32])lds;  // [table][row][strip of the chunk]
+    uint32_t *carry = lds + 2 * 4 * 32;              // [table][row]
+    // scan lane (t, r, j): table t, row r, strip j of the chunk
+    const int st = tid >> 7, sr = (tid >> 5) & 3, sj = tid & 31;
+    if (tid < 8) carry[tid] = 0;
+    for (int q = 0; q * ROW_CHUNK < W; q++) {  // block-uniform
+        const int x = q * ROW_CHUNK + 16 * tid;
+        uint4 px[4];
 #pragma unroll
-    for (int r = 0; r < ROWS_PER_WAVE; r++) px[r] = load16<VEC>(img, ip, W, H, x, y0 + r);
-
-    __shared__ uint32_t stot[2][SAT_BH][SAT_SPQ];   // strip sums of each row
-    __shared__ uint32_t part[2][4][SAT_QW];         // [table][wave][column] 8-row sums
-    __shared__ uint32_t wtot[2][4];                 // wavefront totals of the segment scan
-    uint32_t cI[8];   // 16-bit column sums: cI[2k] columns 4k, 4k+2; cI[2k+1] 4k+1, 4k+3
-    uint32_t cQ[16];
+        for (int r = 0; r < 4; r++) px[r] = load16<VEC>(img, ip, W, H, x, y0 + r);
 #pragma unroll
-    for (int k = 0; k < 8; k++) cI[k] = 0;
+        for (int r = 0; r < 4; r++) {
+            const uint32_t d[4] = {px[r].x, px[r].y, px[r].z, px[r].w};
+            uint32_t a = 0, qq = 0;
 #pragma unroll
-    for (int k = 0; k < 16; k++) cQ[k] = 0;
-#pragma unroll
-    for (int r = 0; r < ROWS_PER_WAVE; r++) {
-        const uint32_t d[4] = {px[r].x, px[r].y, px[r].z, px[r].w};
-        uint32_t a = 0, qq = 0;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            a = dot4u(d[k], 0x01010101u, a);
-            qq = dot4u(d[k], d[k], qq);
-            const uint32_t lo = d[k] & 0x00ff00ffu, hi = (d[k] >> 8) & 0x00ff00ffu;
-            cI[2 * k] += lo;
-            cI[2 * k + 1] += hi;
-            const uint32_t v0 = lo & 0xffffu, v2 = lo >> 16, v1 = hi & 0xffffu, v3 = hi >> 16;
-            cQ[4 * k + 0] = __umul24(v0, v0) + cQ[4 * k + 0];
-            cQ[4 * k + 1] = __umul24(v1, v1) + cQ[4 * k + 1];
-            cQ[4 * k + 2] = __umul24(v2, v2) + cQ[4 * k + 2];
-            cQ[4 * k + 3] = __umul24(v3, v3) + cQ[4 * k + 3];
-        }
-        a = oct_sum_u32(a);
-        qq = oct_sum_u32(qq);
-        if ((l & 7) == 7) {
-            stot[0][ROWS_PER_WAVE * w + r][l >> 3] = a;
-            stot[1][ROWS_PER_WAVE * w + r][l >> 3] = qq;
-        }
-    }
-    // this wavefront's 8-row column sums to LDS
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        *(uint4 *)&part[0][w][16 * l + 4 * k] =
-            make_uint4(cI[2 * k] & 0xffffu, cI[2 * k + 1] & 0xffffu, cI[2 * k] >> 16, cI[2 * k + 1] >> 16);
-        *(uint4 *)&part[1][w][16 * l + 4 * k] =
-            make_uint4(cQ[4 * k], cQ[4 * k + 1], cQ[4 * k + 2], cQ[4 * k + 3]);
-    }
-    __syncthreads();
-
-    // band column sums of columns 4*tid .. +3 of the segment -> running sums
-    // along the segment (thread, then wavefront, then the wavefronts before)
-    uint32_t c[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-        uint4 u = *(const uint4 *)&part[t][0][4 * tid];
-#pragma unroll
-        for (int ww = 1; ww < 4; ww++) {
-            const uint4 v = *(const uint4 *)&part[t][ww][4 * tid];
-            u.x += v.x;
-            u.y += v.y;
-            u.z += v.z;
-            u.w += v.w;
-        }
-        c[t][0] = u.x;
-        c[t][1] = c[t][0] + u.y;
-        c[t][2] = c[t][1] + u.z;
-        c[t][3] = c[t][2] + u.w;
-    }
-    uint32_t tot[2];
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-        const uint32_t inc = wave_incl_scan_u32(c[t][3]);
-        const uint32_t ex = inc - c[t][3];
-#pragma unroll
-        for (int k = 0; k < 4; k++) c[t][k] += ex;
-        tot[t] = inc;
-        if (l == 63) wtot[t][w] = inc;
-    }
-    __syncthreads();
-
-    // band values: bandcol[t][b][x] = sum over the band's rows of the
-    // segment-local row running sum at x
-    const int xs = q * SAT_QW + 4 * tid;
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-        uint32_t off = 0;
-        for (int ww = 0; ww < w; ww++) off += wtot[t][ww];
-        uint32_t *dst = wk.bandcol + ((size_t)t * wk.nBands + b) * W;
-        const uint4 v = make_uint4(c[t][0] + off, c[t][1] + off, c[t][2] + off, c[t][3] + off);
-        if (VEC && xs + 3 < W) {
-            *(uint4 *)(dst + xs) = v;
-        } else {
-            if (xs < W) dst[xs] = v.x;
-            if (xs + 1 < W) dst[xs + 1] = v.y;
-            if (xs + 2 < W) dst[xs + 2] = v.z;
-            if (xs + 3 < W) dst[xs + 3] = v.w;
-        }
-        if (tid == 255) wk.bandseg[((size_t)t * wk.nBands + b) * wk.nSeg + q] = tot[t] + off;
-    }
-
-    // row carries within the segment: for each row, the sum of the segment's
-    // strips left of each strip, and the segment's row total
-    if (tid < 2 * SAT_BH) {
-        const int t = tid / SAT_BH, r = tid % SAT_BH, y = b * SAT_BH + r;
-        if (y < H) {
-            const size_t row = (size_t)t * H + y;
-            uint32_t run = 0;
-#pragma unroll
-            for (int k = 0; k < SAT_SPQ; k++) {
-                const int s = q * SAT_SPQ + k;
-                if (s < wk.nStrips) wk.lrowl[row * wk.nStrips + s] = run;
-                run += stot[t][r][k];
+            for (int k = 0; k < 4; k++) {
+                a = dot4u(d[k], 0x01010101u, a);
+                qq = dot4u(d[k], d[k], qq);
             }
-            wk.segtot[row * wk.nSeg + q] = run;
+            a = oct_sum_u32(a);
+            qq = oct_sum_u32(qq);
+            if ((tid & 7) == 7) {
+                ss[0][r][tid >> 3] = a;
+                ss[1][r][tid >> 3] = qq;
+            }
         }
+        __syncthreads();
+        const uint32_t v = ss[st][sr][sj];
+        uint32_t inc = wave_incl_scan_u32(v);
+        inc -= (tid & 32) ? (uint32_t)__builtin_amdgcn_readlane((int)inc, 31) : 0u;  // two 32-lane scans
+        const uint32_t base = carry[st * 4 + sr];
+        const int strip = q * (ROW_CHUNK / SAT_SW) + sj, y = y0 + sr;
+        if (strip < wk.nS && y < H) wk.lcar[((size_t)st * H + y) * wk.nS + strip] = base + inc - v;
+        __syncthreads();
+        if (sj == 31) carry[st * 4 + sr] = base + inc;
+        __syncthreads();
     }
 }
 
-// -------------------------------------------------------------- top pass --
-// top[t][g][x] = sum over bands b' < b = g*SAT_SUB of (bandcol[t][b'][x] +
-// the totals of band b' in the segments left of x's), i.e. the table value
-// on row b*SAT_BH - 1 above downsweep tile row g.  A block takes 64 columns (inside one segment) of one table;
-// its four wavefronts take a quarter of the bands each and meet in LDS.
-// Lane k of a wavefront also carries the segment part of the k-th band of
-// the current chunk, which is the same for every column of the block.
-// Loads use clamped in-bounds indices so that a whole chunk issues at once.
-constexpr int TOP_COLS = 64;
-constexpr int TOP_CHUNK = 32;  // bands held in registers at a time
-
-struct TopChunk {
-    uint32_t v[TOP_CHUNK];  // bandcol of bands k0 .. k0+31 at this lane's column
-    uint64_t sp;            // lane k: segment part of band k0 + k
-};
-
-__device__ __forceinline__ void top_load(TopChunk &ch, const uint32_t *__restrict__ bc,
-                                         const uint32_t *__restrict__ bs, int W, int nB,
-                                         int nSeg, int seg, int xc, int bfirst, int n, int lane) {
-#pragma unroll
-    for (int k = 0; k < TOP_CHUNK; k++) {
-        const int bb = min(bfirst + k, nB - 1);
-        const uint32_t u = bc[(size_t)bb * W + xc];
-        ch.v[k] = k < n ? u : 0u;
-    }
-    const int bb = min(bfirst + lane, nB - 1);
-    uint64_t sp = 0;
-    for (int s0 = 0; s0 < seg; s0 += 4) {  // 4 loads in flight together
-        uint32_t u4[4];
-#pragma unroll
-        for (int k = 0; k < 4; k++) u4[k] = bs[(size_t)bb * nSeg + min(s0 + k, seg - 1)];
-#pragma unroll
-        for (int k = 0; k < 4; k++) sp += s0 + k < seg ? u4[k] : 0u;
-    }
-    ch.sp = (lane < n && lane < TOP_CHUNK) ? sp : 0u;  // lanes past the chunk: next chunk's bands
-}
-
-// Row sums of the segments left of each segment, for one row rr of [2][H]
-// (table, row): segpre[t][q][y] = sum of segtot[t][y][q'] over q' < q.
-// Four segments at a time, every load of a batch issued before the first
-// use; lanes take consecutive rows, so each store of a wavefront is 256
-// contiguous bytes.
-__device__ __forceinline__ void top_seg_prefix(const SatWork &wk, int H, int rr) {
-    const int nSeg = wk.nSeg, t = rr >= H, y = rr - t * H;
-    const uint32_t *__restrict__ st = wk.segtot + (size_t)rr * nSeg;
-    uint32_t *__restrict__ sp = wk.segpre + (size_t)t * nSeg * H + y;
-    uint32_t run = 0;
-    for (int q0 = 0; q0 < nSeg; q0 += 4) {
-        uint32_t v[4];
-#pragma unroll
-        for (int k = 0; k < 4; k++) v[k] = st[min(q0 + k, nSeg - 1)];
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            if (q0 + k < nSeg) sp[(size_t)(q0 + k) * H] = run;
-            run += v[k];
-        }
-    }
-}
-
-__global__ __launch_bounds__(256) void sat_top(int W, int H, SatWork wk) {
-    const int colBlocks = (W + TOP_COLS - 1) / TOP_COLS;
-    if ((int)blockIdx.x >= 2 * colBlocks) {  // block-uniform: the row blocks
-        const int rr = ((int)blockIdx.x - 2 * colBlocks) * 256 + (int)threadIdx.x;
-        if (rr < 2 * H) top_seg_prefix(wk, H, rr);
-        return;
-    }
-    const int t = blockIdx.x / colBlocks, cb = blockIdx.x % colBlocks;
-    const int tid = threadIdx.x, c = tid & (TOP_COLS - 1), qtr = tid / TOP_COLS;
-    const int x = cb * TOP_COLS + c, xc = min(x, W - 1);
-    const int seg = cb * TOP_COLS / SAT_QW;
-    const int nB = wk.nBands, nSeg = wk.nSeg;
-    const uint32_t *__restrict__ bc = wk.bandcol + (size_t)t * nB * W;
-    const uint32_t *__restrict__ bs = wk.bandseg + (size_t)t * nB * nSeg;
-    uint64_t *__restrict__ top = wk.top + (size_t)t * ((nB + SAT_SUB - 1) / SAT_SUB) * W;
-    const int per = (nB + 3) / 4, b0 = qtr * per;
-    const int nb = min(per, max(nB - b0, 0));  // bands of this quarter
-
-    __shared__ uint64_t qs[4][TOP_COLS];
-    __shared__ uint64_t qseg[4];
-    TopChunk ch;
-    uint64_t colrun = 0, segrun = 0;
-    for (int k0 = 0; k0 < per; k0 += TOP_CHUNK) {  // block-uniform trip count
-        top_load(ch, bc, bs, W, nB, nSeg, seg, xc, b0 + k0, nb - k0, c);
-#pragma unroll
-        for (int k = 0; k < TOP_CHUNK; k++) colrun += ch.v[k];
-        segrun += wave_incl_scan_u64(ch.sp);  // lane 63 ends with the chunk total
-    }
-    qs[qtr][c] = colrun;
-    if (c == 63) qseg[qtr] = segrun;
-    __syncthreads();
-    uint64_t base = 0;
-    for (int q2 = 0; q2 < qtr; q2++) base += qs[q2][c] + qseg[q2];
-    for (int k0 = 0; k0 < per; k0 += TOP_CHUNK) {
-        if (per > TOP_CHUNK)  // more than one chunk: reload (one chunk stays in registers)
-            top_load(ch, bc, bs, W, nB, nSeg, seg, xc, b0 + k0, nb - k0, c);
-        const uint64_t spi = wave_incl_scan_u64(ch.sp);
-        const uint64_t spx = spi - ch.sp;  // lane k: segment part of the chunk's bands before k
-#pragma unroll
-        for (int k = 0; k < TOP_CHUNK; k++) {
-            const uint64_t sk = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(spx >> 32), k) << 32) |
-                                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)spx, k);
-            const int bb = b0 + k0 + k;
-            if (k < nb - k0 && x < W && bb % SAT_SUB == 0) top[(size_t)(bb / SAT_SUB) * W + x] = base + sk;
-            base += ch.v[k];
-        }
-        base += (uint64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(spi >> 32), 63) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)spi, 63));
-    }
+template <bool VEC>
+__global__ __launch_bounds__(256) void sat_tiles(const uint8_t *__restrict__ img, int W, int H, size_t ip,
+                                                 SatWork wk) {
+    __shared__ uint32_t lds[2 * 16 * SAT_SW + 4];
+    const int ntiles = wk.nS * wk.nG;
+    if ((int)blockIdx.x < ntiles)  // block-uniform
+        tile_sums<VEC>(img, W, H, ip, wk, (int)blockIdx.x % wk.nS, (int)blockIdx.x / wk.nS, lds);
+    else
+        row_prefixes<VEC>(img, W, H, ip, wk, (int)blockIdx.x - ntiles, lds);
 }
 
 // ------------------------------------------------------------- downsweep --
@@ -368,46 +257,104 @@ struct BandIn {
 
 // Left carries of every row a wavefront writes in its tile, one per lane:
 // lane 32t + 8k + r holds, for table t, the row sum of all columns left of
-// the strip on row r of the wavefront's part of band k (the segment-local
-// carry plus the segments to the left).  Loaded and added once, before the
+// the strip on row r of the wavefront's part of band k (rows past the image
+// read the last row; their values are not used).  Loaded once, before the
 // first band: within the band loop a use of a just-loaded value would wait
 // for every load issued before it, the next band's bytes included.
 static_assert(2 * SAT_SUB * WAVE_ROWS <= 64, "one left carry per lane");
-__device__ __forceinline__ uint32_t tile_left_carries(const SatWork &wk, int H, int s, int ytile, int w,
-                                                      int l) {
+__device__ __forceinline__ uint32_t tile_left_carries(const SatWork &wk, int H, int s, int ytile, int w, int l) {
     const int t = l >> 5, k = (l / WAVE_ROWS) % SAT_SUB, r = l % WAVE_ROWS;
     const size_t y = (size_t)min(ytile + k * SAT_BH + w * WAVE_ROWS + r, H - 1);
-    const size_t seg = s / SAT_SPQ;
-    return wk.lrowl[((size_t)t * H + y) * wk.nStrips + s] + wk.segpre[((size_t)t * wk.nSeg + seg) * H + y];
+    return wk.lcar[((size_t)t * H + y) * wk.nS + s];
 }
 
 template <bool VEC>
 __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__ img, int W, int H, size_t ip,
                                                      SatWork wk, int64_t *__restrict__ S,
                                                      int64_t *__restrict__ Q) {
-    const int nTy = (wk.nBands + SAT_SUB - 1) / SAT_SUB;
-    const int tix = xcd_tile((int)blockIdx.x, wk.nStrips * nTy);
+    const int nS = wk.nS, nG = wk.nG;
+    const int tix = xcd_tile((int)blockIdx.x, nS * nG);
     if (tix < 0) return;
-    const int s = tix % wk.nStrips, g = tix / wk.nStrips;
+    const int s = tix % nS, g = tix / nS;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int x = s * SAT_SW + 2 * l;
-    const int ytile = g * SAT_SUB * SAT_BH;
+    const int ytile = g * SAT_TR;
 
-    // column carries: the table values on the row above the tile
-    uint64_t s1a, s1b, s2a, s2b;
+    // Table values on the row above the tile, for this lane's columns x and
+    // x + 1 (column c = x - s*SAT_SW):
+    //   sum over tile rows g' < g of colsum[g'] at columns s*SAT_SW .. x
+    //   + sum over g' < g, s' < s of btot[g'][s'].
+    // Wavefront w adds the column sums of tile rows w, w+4, ...; the block
+    // totals are spread over all 256 threads (four per 16-byte load).
+    // Every load of a batch is issued before the first use (clamped
+    // indices, masked sums): a use waits for all loads issued before it.
+    const size_t pcs = (size_t)nS * SAT_SW;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    uint64_t a0 = 0, a1 = 0, q0 = 0, q1 = 0;  // [table][column parity]
+    for (int i0 = wu; i0 < g; i0 += 4 * PRO_BATCH) {  // wavefront-uniform
+        uint2 u[PRO_BATCH], v[PRO_BATCH];
+#pragma unroll
+        for (int k = 0; k < PRO_BATCH; k++) {
+            const size_t gg = (size_t)min(i0 + 4 * k, g - 1);
+            u[k] = *(const uint2 *)(wk.colsum + gg * pcs + x);
+            v[k] = *(const uint2 *)(wk.colsum + ((size_t)nG + gg) * pcs + x);
+        }
+#pragma unroll
+        for (int k = 0; k < PRO_BATCH; k++) {
+            const bool in = i0 + 4 * k < g;
+            a0 += in ? u[k].x : 0u;
+            a1 += in ? u[k].y : 0u;
+            q0 += in ? v[k].x : 0u;
+            q1 += in ? v[k].y : 0u;
+        }
+    }
+    uint64_t bl = 0;  // block totals above-left, table tid >> 7
     {
-        const uint64_t *tp1 = wk.top + (size_t)g * W;
-        const uint64_t *tp2 = wk.top + ((size_t)nTy + g) * W;
-        const int xa = min(x, W - 1), xb = min(x + 1, W - 1);
-        s1a = tp1[xa];
-        s1b = tp1[xb];
-        s2a = tp2[xa];
-        s2b = tp2[xb];
+        const int sq = (s + 3) >> 2, n = g * sq, bt = tid >> 7;
+        for (int i0 = 0; i0 < n; i0 += 128 * PRO_BATCH_B) {  // workgroup-uniform
+            uint4 u[PRO_BATCH_B];
+            int qk[PRO_BATCH_B];
+#pragma unroll
+            for (int k = 0; k < PRO_BATCH_B; k++) {
+                const int i = min(i0 + (tid & 127) + 128 * k, n - 1), gg = i / sq;
+                qk[k] = i - gg * sq;
+                u[k] = *(const uint4 *)(wk.btot + ((size_t)bt * nG + gg) * wk.nS4 + 4 * qk[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < PRO_BATCH_B; k++) {
+                const bool in = i0 + (tid & 127) + 128 * k < n;
+                const int c0 = 4 * qk[k];
+                bl += (in && c0 + 0 < s ? u[k].x : 0u) + (uint64_t)(in && c0 + 1 < s ? u[k].y : 0u) +
+                      (uint64_t)(in && c0 + 2 < s ? u[k].z : 0u) + (uint64_t)(in && c0 + 3 < s ? u[k].w : 0u);
+            }
+        }
     }
     const uint32_t lcar = tile_left_carries(wk, H, s, ytile, w, l);
     BandIn<VEC> cur, nxt;
     cur.load(img, ip, W, H, x, ytile + w * WAVE_ROWS);
-
+    __shared__ uint64_t pro[4][4][64];  // [wave][table*2 + parity][lane] partial column sums
+    __shared__ uint64_t blw[4];           // [wave] partial block totals
+    pro[w][0][l] = a0;
+    pro[w][1][l] = a1;
+    pro[w][2][l] = q0;
+    pro[w][3][l] = q1;
+    {
+        const uint64_t sc = wave_incl_scan_u64(bl);
+        if (l == 63) blw[w] = sc;
+    }
+    __syncthreads();
+    uint64_t s1a, s1b, s2a, s2b;
+    {
+        uint64_t c[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) c[j] = pro[0][j][l] + pro[1][j][l] + pro[2][j][l] + pro[3][j][l];
+        const uint64_t i1 = wave_incl_scan_u64(c[0] + c[1]), i2 = wave_incl_scan_u64(c[2] + c[3]);
+        const uint64_t L1 = blw[0] + blw[1], L2 = blw[2] + blw[3];
+        s1b = i1 + L1;
+        s1a = s1b - c[1];
+        s2b = i2 + L2;
+        s2a = s2b - c[3];
+    }
     __shared__ uint64_t part[2][4][4][64];  // [band parity][wave][value][lane]
     typedef long long v2l __attribute__((ext_vector_type(2)));
     const bool pair = VEC && x + 1 < W;
@@ -761,34 +708,30 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
 
 }  // namespace
 
+// Build scratch of the two-pass build for an H x W image: colsum
+// [2][nG][nS*SAT_SW], btot [2][nG][nS4] (nS4 = nS rounded up to 4) and lcar
+// [2][H][nS], all uint32 (about 0.07 bytes per pixel).
 size_t sat_work_bytes(int W, int H) {
-    const size_t nS = (W + SAT_SW - 1) / SAT_SW, nB = (H + SAT_BH - 1) / SAT_BH;
-    const size_t nQ = (W + SAT_QW - 1) / SAT_QW;
+    const size_t nS = (W + SAT_SW - 1) / SAT_SW, nG = (H + SAT_TR - 1) / SAT_TR, nS4 = (nS + 3) & ~(size_t)3;
     size_t bytes = 0;
     auto add = [&](size_t n) { bytes += (n + 255) & ~(size_t)255; };
-    add(2 * (size_t)H * nS * 4);  // lrowl
-    add(2 * (size_t)H * nQ * 4);  // segtot
-    add(2 * (size_t)H * nQ * 4);  // segpre
-    add(2 * nB * W * 4);          // bandcol
-    add(2 * nB * nQ * 4);         // bandseg
-    add(2 * ((nB + SAT_SUB - 1) / SAT_SUB) * W * 8);  // top
+    add(2 * nG * nS * SAT_SW * 4);  // colsum
+    add(2 * nG * nS4 * 4);          // btot
+    add(2 * (size_t)H * nS * 4);    // lcar
     return bytes;
 }
 
 SatWork sat_work_carve(void *base, int W, int H) {
     SatWork wk;
-    wk.nStrips = (W + SAT_SW - 1) / SAT_SW;
-    wk.nBands = (H + SAT_BH - 1) / SAT_BH;
-    wk.nSeg = (W + SAT_QW - 1) / SAT_QW;
-    const size_t nS = wk.nStrips, nB = wk.nBands, nQ = wk.nSeg;
+    wk.nS = (W + SAT_SW - 1) / SAT_SW;
+    wk.nG = (H + SAT_TR - 1) / SAT_TR;
+    wk.nS4 = (wk.nS + 3) & ~3;
+    const size_t nS = wk.nS, nG = wk.nG;
     char *p = (char *)base;
     auto take = [&](size_t n) { char *q = p; p += (n + 255) & ~(size_t)255; return (void *)q; };
-    wk.lrowl = (uint32_t *)take(2 * (size_t)H * nS * 4);
-    wk.segtot = (uint32_t *)take(2 * (size_t)H * nQ * 4);
-    wk.segpre = (uint32_t *)take(2 * (size_t)H * nQ * 4);
-    wk.bandcol = (uint32_t *)take(2 * nB * W * 4);
-    wk.bandseg = (uint32_t *)take(2 * nB * nQ * 4);
-    wk.top = (uint64_t *)take(2 * ((nB + SAT_SUB - 1) / SAT_SUB) * W * 8);
+    wk.colsum = (uint32_t *)take(2 * nG * nS * SAT_SW * 4);
+    wk.btot = (uint32_t *)take(2 * nG * (size_t)wk.nS4 * 4);
+    wk.lcar = (uint32_t *)take(2 * (size_t)H * nS * 4);
     return wk;
 }
 
@@ -823,26 +766,20 @@ hipError_t sat_build_launch(const uint8_t *img, int W, int H, size_t ip, int64_t
                                nTiles, S, Q);
         return hipGetLastError();
     }
-    // aligned 16-byte image rows (and band rows) for the row pass; even
-    // widths and 16-byte table rows for the paired loads and stores of the
-    // downsweep
+    // aligned 16-byte image rows for the tile pass; even widths and 16-byte
+    // table rows for the paired loads and stores of the downsweep
     const bool rvec = (W % 16 == 0) && (ip % 16 == 0) && (((uintptr_t)img & 15) == 0);
     const bool dvec = (W % 2 == 0) && (ip % 2 == 0) && (((uintptr_t)img & 1) == 0) &&
                       (((uintptr_t)S & 15) == 0) && (((uintptr_t)Q & 15) == 0);
     dim3 block(256);
-    dim3 rgrid(wk.nSeg * wk.nBands);
+    const unsigned blocks = (unsigned)wk.nS * (unsigned)wk.nG + (unsigned)((H + 3) / 4);
     if (rvec)
-        hipLaunchKernelGGL(sat_rows<true>, rgrid, block, 0, st, img, W, H, ip, wk);
+        hipLaunchKernelGGL(sat_tiles<true>, dim3(blocks), block, 0, st, img, W, H, ip, wk);
     else
-        hipLaunchKernelGGL(sat_rows<false>, rgrid, block, 0, st, img, W, H, ip, wk);
+        hipLaunchKernelGGL(sat_tiles<false>, dim3(blocks), block, 0, st, img, W, H, ip, wk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int rowBlocks = (2 * H + 255) / 256;
-    hipLaunchKernelGGL(sat_top, dim3(2 * ((W + TOP_COLS - 1) / TOP_COLS) + rowBlocks), block, 0, st, W,
-                       H, wk);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 grid(xcd_grid(wk.nStrips * ((wk.nBands + SAT_SUB - 1) / SAT_SUB)));
+    dim3 grid(xcd_grid(wk.nS * wk.nG));
     if (dvec)
         hipLaunchKernelGGL(sat_downsweep<true>, grid, block, 0, st, img, W, H, ip, wk, S, Q);
     else
