@@ -7,7 +7,10 @@ summed-area tables (ncc_sat_build: S and Q, int64) and correlate
 resident in device memory before timing starts.
 
 Printed: ONE JSON line.  `value` is coefficients per second of whole steps
-(Gcoeff/s): K steps run back to back between two device synchronisations.
+(Gcoeff/s), end to end: K steps -- each the table build and the correlation,
+which is handed the tables just built -- run back to back between two device
+synchronisations.  The correlation alone (its coefficients per second with the
+tables already built) is `correlation_only`.
 `roofline` covers the step's dominant kernel; its duration comes from HIP
 events recorded around every call in a second pass of K steps (events between
 calls keep kernels from overlapping, so that pass is not used for the step
@@ -22,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -152,35 +156,82 @@ def measured_peaks(stream, d):
         "method": "rates of libncc_peaks.so microbenchmarks (events around back-to-back launches)"}
 
 
-def cpu_baseline(img, tpl, budget_s=12.0):
-    """The oracle (plain C, OpenMP over output rows) on the first R output rows
-    of the headline image, R sized so the run takes about budget_s."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _median_s(fn, reps=3):
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def cpu_baseline(img, tpl, sat_img, bank_img, bank_tpl, per_run_s=1.0):
+    """The oracle (plain C, gcc without fast-math, OpenMP over output rows),
+    timed on the host: median wall time of 3 runs of each sample below, each
+    sample sized from a short probe to take about per_run_s.
+      - correlate on the headline image with all cores (the reported value)
+        and with one thread, on its first R output rows;
+      - the table build of the 4096 x 4096 uniform image, whole (one thread:
+        the oracle's build has no parallel loop);
+      - correlate of the 64-template bank, all cores, first R output rows."""
     import numpy as np
     import oracle
     oracle.build(force=False)
-    threads = oracle.threads(0)
-    hT, wT = tpl.shape[-2:]
-    Wo = img.shape[1] - wT + 1
+    allc = oracle.threads(0)
+    Wo = img.shape[1] - tpl.shape[-1] + 1
 
-    def run(rows):
-        sub = np.ascontiguousarray(img[: rows + hT - 1])
+    def rows_rate(im, tp, nthreads):
+        n, hT, wT = (1,) + tp.shape if tp.ndim == 2 else tp.shape
+        run = lambda r: oracle.correlate(np.ascontiguousarray(im[: r + hT - 1]), tp, want_sums=False,
+                                         nthreads=nthreads)
+        probe = 8
         t0 = time.perf_counter()
-        oracle.correlate(sub, tpl, want_sums=False)
-        return time.perf_counter() - t0
+        run(probe)
+        tp_ = max(time.perf_counter() - t0, 1e-6)
+        rows = int(max(probe, min(im.shape[0] - hT + 1, probe * per_run_s / tp_)))
+        t = _median_s(lambda: run(rows))
+        co = n * rows * (im.shape[1] - wT + 1)
+        return co / t / 1e9, rows, co, t
 
-    probe_rows = 16
-    tp = run(probe_rows)
-    rows = int(max(probe_rows, min(img.shape[0] - hT + 1, probe_rows * budget_s / max(tp, 1e-6))))
-    t = run(rows)
-    coeffs = rows * Wo
+    v_all, r_all, c_all, t_all = rows_rate(img, tpl, 0)
+    v_one, r_one, c_one, t_one = rows_rate(img, tpl, 1)
+    v_bank, r_bank, c_bank, t_bank = rows_rate(bank_img, bank_tpl, 0)
+    t_sat = _median_s(lambda: oracle.sat_build(sat_img))
+    sat_bytes = sat_img.size * 17
     return {
-        "value": round(coeffs / t / 1e9, 6),
+        "value": round(v_all, 6),
         "unit": "Gcoeff/s",
-        "cores": threads,
+        "cores": allc,
         "kind": "oracle",
         "sample": "oracle_correlate (its own table build + per-window loops, int64/double) on the "
                   "first %d output rows x %d columns of the headline 4096x4096 image, 16x16 "
-                  "template: %d coefficients in %.2f s on %d threads" % (rows, Wo, coeffs, t, threads),
+                  "template: %d coefficients, median %.3f s of 3 runs on %d threads"
+                  % (r_all, Wo, c_all, t_all, allc),
+        "cpu_model": _cpu_model(),
+        "compiler": "gcc " + " ".join(oracle.CFLAGS),
+        "statistic": "median wall time (time.perf_counter) of 3 runs per sample",
+        "single_thread": {"value": round(v_one, 6), "unit": "Gcoeff/s", "cores": 1,
+                          "sample": "the same call on the first %d output rows: %d coefficients, "
+                                    "median %.3f s" % (r_one, c_one, t_one)},
+        "sat_build": {"value": round(sat_bytes / t_sat / 1e9, 3), "unit": "GB/s", "cores": 1,
+                      "ms": round(t_sat * 1e3, 2),
+                      "sample": "oracle_sat_build of the whole 4096x4096 uniform image (S and Q "
+                                "int64; 17 algorithmic bytes per pixel), median of 3"},
+        "bank": {"value": round(v_bank, 6), "unit": "Gcoeff/s", "cores": allc,
+                 "sample": "oracle_correlate of the 64-template bank on the first %d output rows: "
+                           "%d coefficients, median %.3f s" % (r_bank, c_bank, t_bank)},
     }
 
 
@@ -208,7 +259,7 @@ def run_loop(args, L, sh, d):
         fns = [lambda: dst.copy_(src)]
     else:
         name = {"sat": "sat", "box": "sat", "corr": "headline", "rect": "headline",
-                "large": "headline", "bank": "bank", "medium": "medium"}[args.loop]
+                "large": "headline", "tables": "headline", "bank": "bank", "medium": "medium"}[args.loop]
         w = synth.make(name)
         img = torch.from_numpy(w["img"]).to(d)
         H, W = img.shape
@@ -223,12 +274,20 @@ def run_loop(args, L, sh, d):
                 fns = [lambda: L.ncc_sat_build(img.data_ptr(), W, H, S.data_ptr(), Q.data_ptr(), sh)]
             else:
                 fns = [lambda: L.ncc_box(S.data_ptr(), W, H, rects.data_ptr(), n, out.data_ptr(), sh)]
+        elif args.loop == "tables":
+            # a 128 x 128 template (the FFT numerator route) given the image's
+            # tables, built once here: the calls themselves build none
+            ltpl = torch.from_numpy(np.ascontiguousarray(w["img"][100:228, 200:328])[None]).to(d)
+            lcoef = torch.empty((1, H - 127, W - 127), dtype=torch.float32, device=d)
+            assert L.ncc_sat_build(img.data_ptr(), W, H, S.data_ptr(), Q.data_ptr(), sh) == 0
+            fns = [lambda: L.ncc_correlate(img.data_ptr(), W, H, ltpl.data_ptr(), 128, 128, 1, None,
+                                           lcoef.data_ptr(), S.data_ptr(), Q.data_ptr(), sh)]
         elif args.loop == "large":
             # a 128 x 128 template: the FFT numerator route
             ltpl = torch.from_numpy(np.ascontiguousarray(w["img"][100:228, 200:328])[None]).to(d)
             lcoef = torch.empty((1, H - 127, W - 127), dtype=torch.float32, device=d)
             fns = [lambda: L.ncc_correlate(img.data_ptr(), W, H, ltpl.data_ptr(), 128, 128, 1, None,
-                                           lcoef.data_ptr(), sh)]
+                                           lcoef.data_ptr(), None, None, sh)]
         elif args.loop == "rect":
             tpl = torch.from_numpy(w["tpl"]).to(d)
             _, hT, wT = tpl.shape
@@ -238,13 +297,13 @@ def run_loop(args, L, sh, d):
                 rc_ = torch.empty((1, rh, rw), dtype=torch.float32, device=d)
                 fns.append(lambda x0=x0, y0=y0, rw=rw, rh=rh, rc_=rc_: L.ncc_correlate_rect(
                     img.data_ptr(), W, H, W, tpl.data_ptr(), wT, hT, 1, x0, y0, rw, rh, rw, None,
-                    rc_.data_ptr(), sh))
+                    rc_.data_ptr(), None, None, sh))
         else:
             tpl = torch.from_numpy(w["tpl"]).to(d)
             nt, hT, wT = tpl.shape
             coef = torch.empty((nt, H - hT + 1, W - wT + 1), dtype=torch.float32, device=d)
             fns = [lambda: L.ncc_correlate(img.data_ptr(), W, H, tpl.data_ptr(), wT, hT, nt, None,
-                                           coef.data_ptr(), sh)]
+                                           coef.data_ptr(), None, None, sh)]
     if args.ramp > 0:
         ramp(fns, args.ramp)
     for _ in range(args.warmup):
@@ -267,7 +326,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="time only the headline step (used under the profiler)")
-    ap.add_argument("--loop", choices=["sat", "corr", "bank", "box", "rect", "large", "medium", "copy"],
+    ap.add_argument("--loop", choices=["sat", "corr", "bank", "box", "rect", "large", "tables", "medium",
+                                       "copy"],
                     help="profiling aid: run one call type --steps times after --warmup and "
                          "exit without the JSON line (copy: a plain 256 MiB device copy, the "
                          "reference for scaling HBM byte counters)")
@@ -313,7 +373,7 @@ def main():
             raise RuntimeError("ncc_sat_build: %d" % rc)
 
     def corr():
-        rc = L.ncc_correlate(pi, W, H, pt, wT, hT, 1, None, pc, sh)
+        rc = L.ncc_correlate(pi, W, H, pt, wT, hT, 1, None, pc, pS, pQ, sh)
         if rc:
             raise RuntimeError("ncc_correlate: %d" % rc)
 
@@ -337,19 +397,25 @@ def main():
     corr_mfma_ops = coeffs * 2048
     corr_bytes = H * W + coeffs * 4  # image read once, coefficients written once
     sat_rate = sat_bytes / (t_sat * 1e-3) / 1e9
-    corr_rate = corr_ops / (t_corr * 1e-3) / 1e12
     corr_gbs = corr_bytes / (t_corr * 1e-3) / 1e9
+    corr_useful = corr_ops / (t_corr * 1e-3) / 1e12
+    corr_issued = corr_mfma_ops / (t_corr * 1e-3) / 1e12
     comp = {
         "ncc_sat_build": {"ms": round(t_sat, 5), "GB/s": round(sat_rate, 1),
                           "frac_hbm": round(sat_rate / HBM_PEAK_GBS, 4),
-                          "kernels": "sat_rows, sat_top, sat_downsweep"},
+                          "kernels": "sat_tiles, sat_downsweep"},
+        # corr_toeplitz: int8 matrix cores; its binding roof is HBM (image +
+        # coefficients, 10.4 us at 8 TB/s), well below its matrix-core roof
         "ncc_correlate": {"ms": round(t_corr, 5), "Gcoeff/s": round(coeffs / (t_corr * 1e-3) / 1e9, 1),
+                          "kernels": "corr_toeplitz<16,32> (int8 matrix cores, 32-row strips)",
+                          "bound": "hbm",
                           "hbm_GB/s": round(corr_gbs, 1), "frac_hbm": round(corr_gbs / HBM_PEAK_GBS, 4),
-                          "int8_mfma_TOP/s_issued": round(corr_mfma_ops / (t_corr * 1e-3) / 1e12, 1),
-                          "frac_mfma": round(corr_mfma_ops / (t_corr * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
-                          "useful_TOP/s": round(corr_rate, 2),
-                          "frac_dot4_roof": round(corr_rate / DOT4_PEAK_TOPS, 4),
-                          "kernels": "corr_toeplitz<16,32> (int8 matrix cores, 32-row strips)"},
+                          "int8_mfma_TOP/s_useful": round(corr_useful, 1),
+                          "frac_mfma_useful": round(corr_useful / INT8_MFMA_PEAK_TOPS, 4),
+                          "int8_mfma_TOP/s_issued": round(corr_issued, 1),
+                          "frac_mfma_issued": round(corr_issued / INT8_MFMA_PEAK_TOPS, 4),
+                          "roofs_us": {"hbm": round(corr_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+                                       "int8_mfma_issued": round(corr_mfma_ops / (INT8_MFMA_PEAK_TOPS * 1e12) * 1e6, 2)}},
     }
     if t_corr >= t_sat:
         roof = {"kernel": "corr_toeplitz<16,32> (ncc_correlate, one launch)", "bound": "hbm",
@@ -357,7 +423,7 @@ def main():
                 "frac": round(corr_gbs / HBM_PEAK_GBS, 4),
                 "traffic": _traffic("corr_toeplitz_headline", ["toeplitz.hip", "ncc_internal.h"])}
     else:
-        roof = {"kernel": "ncc_sat_build (sat_rows + sat_top + sat_downsweep)", "bound": "hbm",
+        roof = {"kernel": "ncc_sat_build (sat_tiles + sat_downsweep)", "bound": "hbm",
                 "achieved": round(sat_rate, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(sat_rate / HBM_PEAK_GBS, 4),
                 "traffic": _traffic("sat_build_headline", ["sat.hip", "ncc_internal.h"])}
@@ -375,13 +441,20 @@ def main():
         "vs_baseline": None,
         "dtype": "u8",
         "data": "synthetic",
+        "value_definition": "end to end: one step = ncc_sat_build + ncc_correlate given those "
+                            "tables; coefficients per second of whole steps",
+        "correlation_only": {"value": round(coeffs / (t_corr * 1e-3) / 1e9, 2), "unit": "Gcoeff/s",
+                             "definition": "ncc_correlate alone with S, Q already built (its calls "
+                                           "back to back between two events)"},
         "config": {"workload": "headline: 4096x4096 u8 smooth noise (N(128,40^2), 9x9 box blur), one "
                                "16x16 template cut from it; step = ncc_sat_build (S, Q int64) + "
-                               "ncc_correlate (4081x4081 float32 coefficients)",
+                               "ncc_correlate (4081x4081 float32 coefficients) given S, Q",
                    "image": [H, W], "template": [hT, wT], "n_templates": 1,
                    "coefficients_per_step": coeffs},
         "roofline": roof,
         "components": comp,
+        "targets": {"sat_build_frac_hbm>=0.70": sat_rate / HBM_PEAK_GBS >= 0.70,
+                    "correlation_frac_of_binding_roof>=0.50": corr_gbs / HBM_PEAK_GBS >= 0.50},
         # the only figures on the pages (context, not a target): both int64
         # tables of a 4096 x 4096 u8 image on a GeForce RTX 3060
         "pages_context": {"sat_build_ms_rtx3060": {"naive": 6.8, "decoupled_lookback": 2.06,
@@ -396,11 +469,8 @@ def main():
         out["measured_peaks"] = pk
         roof["peak_measured"] = pk["write_GB/s"]
         # the vector-unit streaming kernel on the same call, for comparison
-        os.environ["NCC_CORR_PATH"] = "dot4"
-        try:
+        with ncc.options(route="dot4"):
             t_dot4, = time_each([corr], args.steps, stream)
-        finally:
-            os.environ.pop("NCC_CORR_PATH", None)
         comp["ncc_correlate"]["dot4_route_ms"] = round(t_dot4, 5)
         roof["frac_of_measured"] = round(roof["achieved"] / roof["peak_measured"], 4)
 
@@ -422,12 +492,10 @@ def main():
         t_b, t_q = time_each([sat2, boxes], 20, stream)
         rate = sat_bytes / (t_b * 1e-3) / 1e9
         # the single-pass (look-back) build of the same tables, for comparison
-        os.environ["NCC_SAT_PATH"] = "fused"
-        try:
+        with ncc.options(sat_build="single_pass"):
             time_steps([sat2], 0, 3)
             t_f, = time_each([sat2], 20, stream)
-        finally:
-            os.environ.pop("NCC_SAT_PATH", None)
+            ncc.stream_status()  # raises if a single-pass build reported a failure
         out["sat_workload"] = {
             "workload": "4096x4096 u8 uniform: ncc_sat_build, then 1,000,000 box queries on S and on Q",
             "sat_build_ms": round(t_b, 5), "sat_build_GB/s": round(rate, 1),
@@ -444,7 +512,7 @@ def main():
         pbi, pbt, pbc = bimg.data_ptr(), btpl.data_ptr(), bcoef.data_ptr()
 
         def bank():
-            assert L.ncc_correlate(pbi, W, H, pbt, wT, hT, nb, None, pbc, sh) == 0
+            assert L.ncc_correlate(pbi, W, H, pbt, wT, hT, nb, None, pbc, None, None, sh) == 0
 
         ramp([bank], 0.05)
         t_k, = time_each([bank], 10, stream)
@@ -471,7 +539,7 @@ def main():
 
         def bank_pitched():
             assert L.ncc_correlate_rect(pbi, W, H, W, pbt, wT, hT, nb, 0, 0, Wo, Ho, op, None,
-                                        ppc, sh) == 0
+                                        ppc, None, None, sh) == 0
 
         t_kp, = time_each([bank_pitched], 10, stream)
         for (x, y), t in zip(wb["cut_xy"], range(nb)):
@@ -496,7 +564,7 @@ def main():
 
             def rect(x0=x0, y0=y0, rw=rw, rh=rh, prc=prc):
                 assert L.ncc_correlate_rect(pi, W, H, W, pt, wT, hT, 1, x0, y0, rw, rh, rw, None,
-                                            prc, sh) == 0
+                                            prc, None, None, sh) == 0
 
             ramp([rect], 0.03)
             t_r, = time_each([rect], 50, stream)
@@ -509,22 +577,19 @@ def main():
         # picks for them, against the direct generic kernel forced
         lt_out = {"workload": "4096x4096 headline image, one t x t template cut from it: "
                               "ncc_correlate (table build + FFT numerator), against the direct "
-                              "generic kernel (NCC_CORR_PATH=generic)"}
+                              "generic kernel (route option generic)"}
         for t in (64, 128):
             ltpl = torch.from_numpy(np.ascontiguousarray(img_np[100:100 + t, 200:200 + t])[None]).to(d)
             lcoef = torch.empty((1, H - t + 1, W - t + 1), dtype=torch.float32, device=d)
             plt, plc = ltpl.data_ptr(), lcoef.data_ptr()
 
             def large(t=t, plt=plt, plc=plc):
-                assert L.ncc_correlate(pi, W, H, plt, t, t, 1, None, plc, sh) == 0
+                assert L.ncc_correlate(pi, W, H, plt, t, t, 1, None, plc, None, None, sh) == 0
 
             t_auto, = time_each([large], 10, stream)
             assert abs(float(lcoef[0, 100, 200]) - 1.0) <= 1e-5
-            os.environ["NCC_CORR_PATH"] = "generic"
-            try:
+            with ncc.options(route="generic"):
                 t_dir, = time_each([large], 3, stream)
-            finally:
-                os.environ.pop("NCC_CORR_PATH", None)
             n_co = (H - t + 1) * (W - t + 1)
             lt_out["t%d" % t] = {"fft_ms": round(t_auto, 4), "direct_ms": round(t_dir, 4),
                                  "Gcoeff/s": round(n_co / (t_auto * 1e-3) / 1e9, 1),
@@ -546,15 +611,12 @@ def main():
         pmi, pmt, pmc = mi.data_ptr(), mt.data_ptr(), mcoef.data_ptr()
 
         def medium():
-            assert L.ncc_correlate(pmi, mW, mH, pmt, mwT, mhT, 1, None, pmc, sh) == 0
+            assert L.ncc_correlate(pmi, mW, mH, pmt, mwT, mhT, 1, None, pmc, None, None, sh) == 0
 
         ramp([medium], 0.03)
         t_m, = time_each([medium], 50, stream)
-        os.environ["NCC_CORR_PATH"] = "generic"
-        try:
+        with ncc.options(route="generic"):
             t_mg, = time_each([medium], 10, stream)
-        finally:
-            os.environ.pop("NCC_CORR_PATH", None)
         mmacs = mHo * mWo * mhT * mwT
         out["medium_workload"] = {
             "workload": "1024x1024 u8 smooth noise, one 32x32 template cut with +-8 noise: ncc_correlate",
@@ -566,7 +628,8 @@ def main():
             "generic_route_us": round(t_mg * 1e3, 2)}
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(img_np, tpl_np[0])
+        wsat, wbank = synth.make("sat"), synth.make("bank")
+        out["cpu_baseline"] = cpu_baseline(img_np, tpl_np[0], wsat["img"], wbank["img"], wbank["tpl"])
     print(json.dumps(out), flush=True)
 
 

@@ -28,6 +28,15 @@
  *   - The library keeps a per-device, per-stream workspace cache (growing,
  *     freed by ncc_release).  Calls on one stream are ordered by the stream;
  *     calls on different streams use different workspaces.
+ *   - HIP graphs: a call recorded into a graph during stream capture keeps
+ *     using that stream's workspace when the graph is replayed.  A block
+ *     that a later call outgrows is retired, not freed, so replays stay
+ *     valid until ncc_release (after which graphs must be captured again).
+ *     A replay shares the workspace with every other call made on the
+ *     capturing stream: replays and such calls must not run concurrently.
+ *   - Routes and tuning: process-wide settings of ncc_set_option, read at
+ *     every call; the defaults need no setting.  Nothing is read from the
+ *     environment.
  */
 #ifndef NCC_H
 #define NCC_H
@@ -64,8 +73,17 @@ extern "C" {
  *        columns 0..x (inclusive).
  *   Q    [H][W] int64, device, written: the same sum of I^2.
  *
+ * The default build is two passes with no waiting between workgroups.  The
+ * single-pass build (ncc_set_option(NCC_OPT_SAT_BUILD, NCC_SAT_SINGLE_PASS);
+ * section 15.8's decoupled look-back, one read of the image) has bounded
+ * waits: if one gives up, or the stream's build state was left inconsistent,
+ * the tiles concerned are written as INT64_MIN and the failure is reported
+ * as NCC_EHIP by ncc_stream_status, or by the next call on that stream that
+ * uses the single-pass build, which also resets the state.
+ *
  * Errors: NCC_EINVAL (null pointer, W < 1, H < 1), NCC_ERANGE (W >
- * NCC_MAX_WIDTH, or W*H*65025 past int64), NCC_ENOMEM, NCC_EHIP.
+ * NCC_MAX_WIDTH, or W*H*65025 past int64), NCC_ENOMEM, NCC_EHIP (including
+ * an earlier single-pass failure on this stream, see above).
  */
 int ncc_sat_build(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q,
                   void *stream);
@@ -94,7 +112,8 @@ int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n,
  * ncc_correlate -- valid-mode normalized cross-correlation of an image with
  * one template or a bank of templates ("Image in shared memory":
  * corrShared_kernel's window sums; section 15.8: window sums from the tables
- * by the four-corner rule).
+ * by the four-corner rule, one table serving every window, every template in
+ * a bank and every shift of an FFT search).
  *
  *   img       [H][W] uint8, device.
  *   tpl       [nTpl][hT][wT] uint8, device.
@@ -108,30 +127,38 @@ int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n,
  *               gamma = num / sqrt(varI*varT), and 0 when varI or varT is 0.
  *             num, varI and varT are exact integers; the float evaluation
  *             after them is within 1e-5 of the correctly rounded value.
+ *   S, Q      nullable pair (both or neither); [H][W] int64, device: the
+ *             summed-area tables of img (as ncc_sat_build writes them), read
+ *             only.  NULL: routes that read tables build them in the
+ *             workspace.
  *
- * Window sums SumI and SumISq are exact integers taken from summed-area
- * tables of the image by the four-corner rule (tables of each on-chip image
- * strip for the specialised kernels, the full int64 tables of ncc_sat_build
- * in the workspace otherwise).  A bank (nTpl > 1) of templates with at most
- * 16 rows of at most 16 pixels runs SumIT as an int8 matrix-core
- * contraction; other shapes run per template on the vector units, or, for
- * large templates (where it is estimated faster; about 48 x 48 and up on a
- * 4096 x 4096 image), as a product of 2-D Fourier transforms in double
- * precision whose result is rounded to the integer SumIT it equals (the
- * "FFT numerator" section 15.8 names; images whose padded transform exceeds
- * 8192 x 8192 always run the direct kernel).
+ * Window sums SumI and SumISq are exact integers by the four-corner rule.
+ * The generic and FFT routes read them from the full tables (the caller's S,
+ * Q when given).  The specialised kernels form the same integers from the
+ * image strip they stage on chip (a table of the strip, or per-window sums)
+ * and do not read S, Q: reading four int64 corners of two tables per
+ * position would make them HBM-bound well below their compute rate.  A bank
+ * (nTpl > 1) of templates with at most 16 rows of at most 16 pixels runs
+ * SumIT as an int8 matrix-core contraction; one template of 16 rows and 13
+ * to 16 columns runs on the int8 matrix cores as a banded Toeplitz product
+ * (small launches on the vector units); other templates up to 32 x 64 run on
+ * the vector units; larger ones run the generic kernel or, where estimated
+ * faster (about 48 x 48 and up on a 4096 x 4096 image), a product of 2-D
+ * Fourier transforms in double precision rounded to the integer SumIT it
+ * equals (the "FFT numerator" section 15.8 names; images whose padded
+ * transform exceeds 8192 x 8192 always run the generic kernel).
+ * ncc_set_option(NCC_OPT_CORR_ROUTE, ...) forces a route.
  *
- * Errors: NCC_EINVAL (null img/tpl/coef_out, W or H < 1, wT or hT < 1,
- * wT > W, hT > H, nTpl < 1), NCC_ERANGE (W > NCC_MAX_WIDTH,
- * wT*hT > NCC_MAX_TEMPLATE_PIXELS, outputs past 2^62 bytes),
+ * Errors: NCC_EINVAL (null img/tpl/coef_out, exactly one of S, Q null, W or
+ * H < 1, wT or hT < 1, wT > W, hT > H, nTpl < 1), NCC_ERANGE (W >
+ * NCC_MAX_WIDTH, wT*hT > NCC_MAX_TEMPLATE_PIXELS, outputs past 2^62 bytes),
  * NCC_EUNSUPPORTED (called during stream capture before the stream's
- * workspace was sized by an uncaptured call), NCC_ENOMEM, NCC_EHIP.  Every
- * template shape within the bounds above is supported: templates whose
- * staged image tile exceeds the LDS of one workgroup run in blocks.
+ * workspace was sized by an uncaptured call), NCC_ENOMEM, NCC_EHIP.
  */
 int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl,
                   int wT, int hT, int nTpl, int32_t *sums_out,
-                  float *coef_out, void *stream);
+                  float *coef_out, const int64_t *S, const int64_t *Q,
+                  void *stream);
 
 /* Largest output row pitch of ncc_correlate_rect, in elements. */
 #define NCC_MAX_OUT_PITCH (1 << 24)
@@ -161,15 +188,20 @@ int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl,
  *              (x0+u, y0+v).
  *   coef_out   [nTpl][h][out_pitch] float32, device, likewise (may be NULL
  *              when w or h is 0).
+ *   S, Q       nullable pair; [H][W] int64 summed-area tables of the whole
+ *              H x W image (row pitch W elements, as ncc_sat_build writes
+ *              them for the dense image), read in place by the routes that
+ *              read tables; NULL: those routes build tables of the
+ *              rectangle's windows in the workspace.
  *
  * Every value equals ncc_correlate's at the same position, bit for bit for
  * the sums.  Only the image rows and columns that the rectangle's windows
  * cover are read (the streaming kernel may also read up to 15 bytes on each
  * side of them within the same image row).
  *
- * Errors: NCC_EINVAL (null img/tpl, null coef_out with w, h > 0, W or H < 1,
- * wT or hT < 1, wT > W, hT > H, nTpl < 1, img_pitch < W, w or h < 0,
- * out_pitch < w),
+ * Errors: NCC_EINVAL (null img/tpl, null coef_out with w, h > 0, exactly
+ * one of S, Q null, W or H < 1, wT or hT < 1, wT > W, hT > H, nTpl < 1,
+ * img_pitch < W, w or h < 0, out_pitch < w),
  * NCC_ERANGE (the rectangle outside the valid positions,
  * wT*hT > NCC_MAX_TEMPLATE_PIXELS, w+wT-1 > NCC_MAX_WIDTH,
  * (w+wT-1)*(h+hT-1) > 2^40, img_pitch*H > 2^48,
@@ -179,16 +211,81 @@ int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl,
 int ncc_correlate_rect(const uint8_t *img, int W, int H, size_t img_pitch,
                        const uint8_t *tpl, int wT, int hT, int nTpl,
                        int x0, int y0, int w, int h, size_t out_pitch,
-                       int32_t *sums_out, float *coef_out, void *stream);
+                       int32_t *sums_out, float *coef_out, const int64_t *S,
+                       const int64_t *Q, void *stream);
+
+/*
+ * Options: process-wide settings read at every call (no environment
+ * variables are read).  ncc_set_option returns NCC_OK, or NCC_EINVAL for an
+ * unknown option or value (the setting is then unchanged); ncc_get_option
+ * writes the current value.
+ *
+ *   NCC_OPT_CORR_ROUTE    correlation route: NCC_ROUTE_AUTO (default: the
+ *                         choice described at ncc_correlate), or one forced
+ *                         route: NCC_ROUTE_GENERIC (tables + generic kernel,
+ *                         any shape), NCC_ROUTE_FFT (tables + FFT numerator,
+ *                         images up to 8192 x 8192 padded), NCC_ROUTE_SINGLE
+ *                         (one template at a time; the matrix-core kernel
+ *                         wherever its shape fits), NCC_ROUTE_DOT4 (the
+ *                         vector-unit streaming kernel), NCC_ROUTE_TILE (the
+ *                         vector-unit tile kernel).  A forced route runs
+ *                         every template on its own (no bank kernel); where
+ *                         its kernel does not take the shape, the generic
+ *                         kernel runs (NCC_ROUTE_SINGLE first tries the
+ *                         streaming kernel).
+ *   NCC_OPT_SAT_BUILD     NCC_SAT_TWO_PASS (default) or NCC_SAT_SINGLE_PASS.
+ *   NCC_OPT_TZ_STRIP      rows per workgroup of the matrix-core single-
+ *                         template kernel: 0 (default: chosen per launch),
+ *                         16 or 32.
+ *   NCC_OPT_STREAM_ROWS   rows per workgroup of the vector-unit streaming
+ *                         kernel: 0 (default: chosen per launch), 16, 32, 64.
+ *   NCC_OPT_SAT_SPIN      polls of a single-pass look-back wait before it
+ *                         gives up: >= 0, default 4194304.
+ *   NCC_OPT_SAT_STALE     for tests of the failure report: 1 makes the next
+ *                         single-pass build (on any stream) start from a
+ *                         state whose tile ticket counter is past the end, as
+ *                         a call that never finished would leave it; that
+ *                         build resets the option to 0.  Default 0.
+ */
+#define NCC_OPT_CORR_ROUTE 1
+#define NCC_OPT_SAT_BUILD 2
+#define NCC_OPT_TZ_STRIP 3
+#define NCC_OPT_STREAM_ROWS 4
+#define NCC_OPT_SAT_SPIN 5
+#define NCC_OPT_SAT_STALE 6
+
+#define NCC_ROUTE_AUTO 0
+#define NCC_ROUTE_GENERIC 1
+#define NCC_ROUTE_FFT 2
+#define NCC_ROUTE_SINGLE 3
+#define NCC_ROUTE_DOT4 4
+#define NCC_ROUTE_TILE 5
+
+#define NCC_SAT_TWO_PASS 0
+#define NCC_SAT_SINGLE_PASS 1
+
+int ncc_set_option(int option, int value);
+int ncc_get_option(int option, int *value);
+
+/*
+ * ncc_stream_status -- waits for `stream` and reports a failure of a
+ * single-pass table build enqueued on it since the last report (a bounded
+ * look-back wait that gave up, or a build state left inconsistent): NCC_EHIP
+ * then, after resetting the stream's build state, else NCC_OK; also
+ * NCC_EHIP if the wait itself fails.  Tables written by a failed build hold
+ * INT64_MIN in the tiles concerned (or are not written at all).
+ */
+int ncc_stream_status(void *stream);
 
 /* Static string naming a status code. */
 const char *ncc_strerror(int status);
 
-/* Frees every cached workspace on every device.  Waits for the streams that
- * used them.  Later calls allocate again. */
+/* Frees every cached workspace on every device, including blocks retired by
+ * growth.  Waits for the devices that used them.  Later calls allocate
+ * again; HIP graphs that recorded earlier calls must be captured again. */
 void ncc_release(void);
 
-/* ABI version of this header (major*100 + minor). */
+/* ABI version of this header (major*100 + minor): 200. */
 int ncc_version(void);
 
 #ifdef __cplusplus

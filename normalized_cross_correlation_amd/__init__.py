@@ -15,6 +15,14 @@ the tensor device's current torch stream:
 * ``correlate_rect(img, tpl, x0, y0, w, h)`` -> the same over a w x h rectangle
   of positions, read in place from a row-strided image, written to row-strided
   output
+* ``set_option(name, value)``, ``get_option(name)``, ``options(**settings)``
+  (a context manager restoring the previous values): the process-wide route
+  and tuning options of ``ncc_set_option``
+* ``stream_status()``  -> waits for the current stream; raises NCCError when a
+  single-pass table build on it reported a failure
+
+``correlate`` and ``correlate_rect`` take ``tables=(S, Q)``, summed-area
+tables of the whole image from ``sat_build``, for the routes that read them.
 """
 from __future__ import annotations
 
@@ -22,11 +30,19 @@ import ctypes
 import os
 
 __all__ = ["sat_build", "box", "correlate", "correlate_rect", "release", "lib", "NCCError",
+           "set_option", "get_option", "options", "stream_status", "OPTIONS", "ROUTES",
            "ABI_FUNCTIONS", "LIB_PATH", "MAX_WIDTH", "MAX_TEMPLATE_PIXELS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libncc.so")
 ABI_FUNCTIONS = ("ncc_sat_build", "ncc_box", "ncc_correlate", "ncc_correlate_rect",
+                 "ncc_set_option", "ncc_get_option", "ncc_stream_status",
                  "ncc_strerror", "ncc_release", "ncc_version")
+ABI_VERSION = 200
+# option numbers and values of ncc.h
+OPTIONS = {"route": 1, "sat_build": 2, "tz_strip": 3, "stream_rows": 4, "sat_spin": 5,
+           "sat_stale": 6}
+ROUTES = {"auto": 0, "generic": 1, "fft": 2, "single": 3, "dot4": 4, "tile": 5}
+SAT_BUILDS = {"two_pass": 0, "single_pass": 1}
 MAX_WIDTH = 66051
 MAX_TEMPLATE_PIXELS = 33025
 MAX_OUT_PITCH = 1 << 24
@@ -54,17 +70,26 @@ def lib():
         L.ncc_sat_build.restype = I
         L.ncc_box.argtypes = [P, I, I, P, I64, P, P]
         L.ncc_box.restype = I
-        L.ncc_correlate.argtypes = [P, I, I, P, I, I, I, P, P, P]
+        L.ncc_correlate.argtypes = [P, I, I, P, I, I, I, P, P, P, P, P]
         L.ncc_correlate.restype = I
         Z = ctypes.c_size_t
-        L.ncc_correlate_rect.argtypes = [P, I, I, Z, P, I, I, I, I, I, I, I, Z, P, P, P]
+        L.ncc_correlate_rect.argtypes = [P, I, I, Z, P, I, I, I, I, I, I, I, Z, P, P, P, P, P]
         L.ncc_correlate_rect.restype = I
+        L.ncc_set_option.argtypes = [I, I]
+        L.ncc_set_option.restype = I
+        L.ncc_get_option.argtypes = [I, ctypes.POINTER(I)]
+        L.ncc_get_option.restype = I
+        L.ncc_stream_status.argtypes = [P]
+        L.ncc_stream_status.restype = I
         L.ncc_strerror.argtypes = [I]
         L.ncc_strerror.restype = ctypes.c_char_p
         L.ncc_release.argtypes = []
         L.ncc_release.restype = None
         L.ncc_version.argtypes = []
         L.ncc_version.restype = I
+        if L.ncc_version() != ABI_VERSION:
+            raise RuntimeError("libncc.so ABI %d, binding expects %d: rebuild the library"
+                               % (L.ncc_version(), ABI_VERSION))
         _lib = L
     return _lib
 
@@ -135,11 +160,24 @@ def box(S, rects, out=None):
     return out
 
 
-def correlate(img, tpl, want_sums: bool = False, coef=None, sums=None):
+def _tables(tables, H, W, device):
+    """Device pointers of a (S, Q) pair of [H][W] int64 tables, or (None, None)."""
+    import torch
+    if tables is None:
+        return None, None
+    S, Q = tables
+    for name, t in (("S", S), ("Q", Q)):
+        _dev_tensor(t, torch.int64, name, 2)
+        if tuple(t.shape) != (H, W) or t.device != device:
+            raise ValueError("%s must be [H][W] on the image's device" % name)
+    return S.data_ptr(), Q.data_ptr()
+
+
+def correlate(img, tpl, want_sums: bool = False, coef=None, sums=None, tables=None):
     """Valid-mode NCC of a [H][W] uint8 image with a [hT][wT] template or a
     [n][hT][wT] bank.  Returns (coef float32 [n][Ho][Wo], sums int32
     [2+n][Ho][Wo] or None): sums planes are SumI, SumISq, then SumIT per
-    template."""
+    template.  tables: optional (S, Q) from sat_build(img)."""
     import torch
     _dev_tensor(img, torch.uint8, "img", 2)
     if tpl.dim() == 2:
@@ -161,10 +199,11 @@ def correlate(img, tpl, want_sums: bool = False, coef=None, sums=None):
         _dev_tensor(sums, torch.int32, "sums", 3)
         if tuple(sums.shape) != (2 + n, Ho, Wo):
             raise ValueError("sums must be [2+n][Ho][Wo]")
+    pS, pQ = _tables(tables, H, W, img.device)
     with torch.cuda.device(img.device):
         _check("ncc_correlate", lib().ncc_correlate(
             img.data_ptr(), W, H, tpl.data_ptr(), wT, hT, n,
-            sums.data_ptr() if sums is not None else None, coef.data_ptr(), _stream(img)))
+            sums.data_ptr() if sums is not None else None, coef.data_ptr(), pS, pQ, _stream(img)))
     return coef, sums
 
 
@@ -198,12 +237,13 @@ def _pitched(t, name, planes, h, w):
 
 
 def correlate_rect(img, tpl, x0: int, y0: int, w: int, h: int, want_sums: bool = False,
-                   out_pitch=None, coef=None, sums=None):
+                   out_pitch=None, coef=None, sums=None, tables=None):
     """NCC at the positions x0..x0+w-1 by y0..y0+h-1 only (each window inside
     the image).  img is [H][W] uint8 with dense rows (a row-strided view, e.g.
     a crop, is read in place).  Returns (coef float32 [n][h][w], sums int32
     [2+n][h][w] or None), views of buffers whose rows are out_pitch (default
-    w) elements apart; coef / sums may be given as such views."""
+    w) elements apart; coef / sums may be given as such views.  tables:
+    optional (S, Q), [H][W] tables of the whole image."""
     import torch
     _row_strided(img, torch.uint8, "img", 2)
     if tpl.dim() == 2:
@@ -227,12 +267,62 @@ def correlate_rect(img, tpl, x0: int, y0: int, w: int, h: int, want_sums: bool =
         coef = torch.empty((n, h, out_pitch), dtype=torch.float32, device=img.device)[:, :, :w]
     if want_sums and sums is None:
         sums = torch.empty((2 + n, h, out_pitch), dtype=torch.int32, device=img.device)[:, :, :w]
+    pS, pQ = _tables(tables, H, W, img.device)
     with torch.cuda.device(img.device):
         _check("ncc_correlate_rect", lib().ncc_correlate_rect(
             img.data_ptr(), W, H, ip, tpl.data_ptr(), wT, hT, n, x0, y0, w, h, out_pitch,
             sums.data_ptr() if sums is not None and sums.numel() else None,
-            coef.data_ptr() if coef.numel() else None, _stream(img)))
+            coef.data_ptr() if coef.numel() else None, pS, pQ, _stream(img)))
     return coef, sums
+
+
+def _option_value(name, value):
+    if name == "route" and isinstance(value, str):
+        return ROUTES[value]
+    if name == "sat_build" and isinstance(value, str):
+        return SAT_BUILDS[value]
+    return int(value)
+
+
+def set_option(name: str, value):
+    """Sets a process-wide option: route ("auto", "generic", "fft", "single",
+    "dot4", "tile"), sat_build ("two_pass", "single_pass"), tz_strip (0, 16,
+    32), stream_rows (0, 16, 32, 64), sat_spin (>= 0), sat_stale (0, 1)."""
+    _check("ncc_set_option", lib().ncc_set_option(OPTIONS[name], _option_value(name, value)))
+
+
+def get_option(name: str) -> int:
+    v = ctypes.c_int()
+    _check("ncc_get_option", lib().ncc_get_option(OPTIONS[name], ctypes.byref(v)))
+    return v.value
+
+
+class options:
+    """Context manager: sets the given options, restores the previous values
+    on exit (``with options(route="generic", sat_build="single_pass"): ...``)."""
+
+    def __init__(self, **settings):
+        self.settings = {k: v for k, v in settings.items() if v is not None}
+
+    def __enter__(self):
+        self.old = {k: get_option(k) for k in self.settings}
+        for k, v in self.settings.items():
+            set_option(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            set_option(k, v)
+
+
+def stream_status(device=None):
+    """Waits for the current stream of `device` and raises NCCError if a
+    single-pass table build on it reported a failure (ncc_stream_status)."""
+    import torch
+    d = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(d):
+        _check("ncc_stream_status", lib().ncc_stream_status(
+            ctypes.c_void_p(torch.cuda.current_stream(d).cuda_stream)))
 
 
 def release():

@@ -29,7 +29,6 @@
 // taken in blocks of rows x dwords, each block staging its part of the image.
 #include "ncc_internal.h"
 
-#include <cstdlib>
 
 namespace ncc {
 
@@ -419,24 +418,27 @@ void corr_stream(CorrArgs a, int t, int ntx, int nty) {
 // --------------------------------------------------------------- generic --
 constexpr int GT = 64;  // output tile edge
 
-__device__ __forceinline__ long long sat_box(const int64_t *S, int W, int x0, int y0, int x1,
-                                             int y1) {
-    // 0 <= x0 < x1 <= W, 0 <= y0 < y1 <= H guaranteed by the caller
-    const int64_t *rb = S + (size_t)(y1 - 1) * W;
+// The four-corner rule on a table view: S points at view position (0, 0),
+// rows `pitch` elements apart; (tx, ty) is the view's origin in the table, so
+// a corner left of or above the view is a table element unless it lies left
+// of column 0 or above row 0 of the table, where it reads as zero.
+__device__ __forceinline__ long long sat_box(const int64_t *S, size_t pitch, int tx, int ty, int x0,
+                                             int y0, int x1, int y1) {
+    // 0 <= x0 < x1, 0 <= y0 < y1 inside the view guaranteed by the caller
+    const int64_t *rb = S + (ptrdiff_t)(y1 - 1) * (ptrdiff_t)pitch;
     long long D = rb[x1 - 1];
-    long long C = x0 > 0 ? rb[x0 - 1] : 0;
+    long long C = tx + x0 > 0 ? rb[x0 - 1] : 0;
     long long B = 0, A = 0;
-    if (y0 > 0) {
-        const int64_t *rt = S + (size_t)(y0 - 1) * W;
+    if (ty + y0 > 0) {
+        const int64_t *rt = S + (ptrdiff_t)(y0 - 1) * (ptrdiff_t)pitch;
         B = rt[x1 - 1];
-        A = x0 > 0 ? rt[x0 - 1] : 0;
+        A = tx + x0 > 0 ? rt[x0 - 1] : 0;
     }
     return D - B - C + A;
 }
 
-__global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int64_t *__restrict__ S,
-                                                    const int64_t *__restrict__ Q, int pitch,
-                                                    int rowsT, int jb, int kb) {
+__global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, Tables tb, int pitch, int rowsT,
+                                                    int jb, int kb) {
     extern __shared__ uint32_t tile[];  // rowsT x pitch bytes
     const int tid = threadIdx.x;
     const int ntx = (a.Wo + GT - 1) / GT;  // 1-D grid: any height
@@ -509,8 +511,8 @@ __global__ __launch_bounds__(256) void corr_generic(CorrArgs a, int t, const int
         for (int s = 0; s < 4; s++) {
             const int x = x0 + 4 * tx + s;
             if (x >= a.Wo) break;
-            const long long sumI = sat_box(S, a.W, x, y, x + a.wT, y + a.hT);
-            const long long sumISq = sat_box(Q, a.W, x, y, x + a.wT, y + a.hT);
+            const long long sumI = sat_box(tb.S, tb.pitch, tb.tx, tb.ty, x, y, x + a.wT, y + a.hT);
+            const long long sumISq = sat_box(tb.Q, tb.pitch, tb.tx, tb.ty, x, y, x + a.wT, y + a.hT);
             const long long sumIT = acc[dy][s];
             const long long num = K * sumIT - sumI * ts.sumT;
             const long long varI = K * sumISq - sumI * sumI;
@@ -573,13 +575,11 @@ int device_cus() {
 // rows, one after another, so tall strips waste least on the halo and short
 // ones give more workgroups.  Estimated time ~ (rows per strip) x (waves of
 // workgroups), where fewer workgroups than resident slots still cost one
-// wave; the tallest strip among the cheapest wins.  NCC_STREAM_RS = 16, 32
-// or 64 fixes it instead.
+// wave; the tallest strip among the cheapest wins.  The option
+// NCC_OPT_STREAM_ROWS = 16, 32 or 64 fixes it instead.
 int stream_rs(int Ho, int ntx, int HT) {
-    if (const char *e = std::getenv("NCC_STREAM_RS")) {
-        const int v = std::atoi(e);
-        if (v == 16 || v == 32 || v == 64) return v;
-    }
+    const int v = opt_get(NCC_OPT_STREAM_ROWS);
+    if (v == 16 || v == 32 || v == 64) return v;
     const double slots = (double)device_cus() * STREAM_WG_PER_CU;
     int best = 64;
     double best_cost = 0;
@@ -656,8 +656,7 @@ bool corr_generic_supported(int wT, int hT) {
     return wT >= 1 && hT >= 1;  // any shape: large templates run in blocks
 }
 
-hipError_t corr_generic_launch(const CorrArgs &a, int t, const int64_t *S, const int64_t *Q,
-                               hipStream_t st) {
+hipError_t corr_generic_launch(const CorrArgs &a, int t, const Tables &tb, hipStream_t st) {
     int pitch, rowsT, jb, kb;
     generic_geometry(a.wT, a.hT, &pitch, &rowsT, &jb, &kb);
     size_t lds = (size_t)pitch * rowsT;
@@ -669,7 +668,7 @@ hipError_t corr_generic_launch(const CorrArgs &a, int t, const int64_t *S, const
     });
     if (e != hipSuccess) return e;
     dim3 grid(((a.Wo + GT - 1) / GT) * ((a.Ho + GT - 1) / GT));
-    hipLaunchKernelGGL(corr_generic, grid, dim3(256), lds, st, a, t, S, Q, pitch, rowsT, jb, kb);
+    hipLaunchKernelGGL(corr_generic, grid, dim3(256), lds, st, a, t, tb, pitch, rowsT, jb, kb);
     return hipGetLastError();
 }
 

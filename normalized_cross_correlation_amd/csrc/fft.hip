@@ -312,15 +312,16 @@ __global__ __launch_bounds__(FFT_T) void fft_cols_pass2(const double2 *__restric
 // Z = E + i O, z = M x IDFT(Z)), SumIT = round(scale * sample), then SumI and
 // SumISq by the four-corner rule on the tables and the coefficient, as the
 // generic route does.  The four corners are taken as differences of two
-// table rows staged once in LDS: cS[x] = S(x, y+hT-1) - S(x, y-1) (mod 2^32;
-// every window sum is below 2^32, so its difference of two cS is exact).
-// They reuse the samples' LDS once each lane holds its SumIT values (at most
-// ROW_MAXX of them: Wo <= 8192).
+// table rows staged once in LDS: cS[x + 1] = S(x, y+hT-1) - S(x, y-1) for
+// view columns x = -1 .. W-1 (mod 2^32; every window sum is below 2^32, so
+// its difference of two cS is exact; column -1 and row -1 are table elements
+// when the view starts inside the table, zero at its edges).  cS and cQ reuse
+// the LDS of the samples and the twiddle quarter table (8 (W + 1) <= 24 M
+// bytes) once each lane holds its SumIT values (at most ROW_MAXX of them:
+// Wo <= 8192).
 __global__ __launch_bounds__(ROW_T) void fft_rows_c2r_coef(const double2 *__restrict__ spec,
                                                            int pitch, int eM, double scale,
-                                                           CorrArgs a, int t,
-                                                           const int64_t *__restrict__ S,
-                                                           const int64_t *__restrict__ Q,
+                                                           CorrArgs a, int t, Tables tb,
                                                            const double2 *__restrict__ tw) {
     extern __shared__ double2 z[];  // [M] samples (later cS, cQ [W] each), [M/2] quarter table
     const int M = 1 << eM, y = blockIdx.x;
@@ -343,15 +344,23 @@ __global__ __launch_bounds__(ROW_T) void fft_rows_c2r_coef(const double2 *__rest
         const double2 zz = z[(x < a.Wo ? x : 0) >> 1];
         sit[i] = __double2ll_rn(((x & 1) ? zz.y : zz.x) * scale);
     }
-    __syncthreads();  // the samples are read; their LDS takes cS, cQ
-    uint32_t *cS = (uint32_t *)z, *cQ = cS + a.W;
+    __syncthreads();  // the samples and the quarter table are read; their LDS takes cS, cQ
+    uint32_t *cS = (uint32_t *)z, *cQ = cS + a.W + 1;
     {
-        const int64_t *sb = S + (size_t)(y + a.hT - 1) * a.W, *qb = Q + (size_t)(y + a.hT - 1) * a.W;
-        const int64_t *st = S + (size_t)(y > 0 ? y - 1 : 0) * a.W;
-        const int64_t *qt = Q + (size_t)(y > 0 ? y - 1 : 0) * a.W;
-        for (int x = threadIdx.x; x < a.W; x += ROW_T) {
-            cS[x] = (uint32_t)(sb[x] - (y > 0 ? st[x] : 0));
-            cQ[x] = (uint32_t)(qb[x] - (y > 0 ? qt[x] : 0));
+        const ptrdiff_t pt = (ptrdiff_t)tb.pitch;
+        const int64_t *sb = tb.S + (ptrdiff_t)(y + a.hT - 1) * pt, *qb = tb.Q + (ptrdiff_t)(y + a.hT - 1) * pt;
+        const bool above = tb.ty + y > 0;  // the row above the windows is a table row
+        const int64_t *st = tb.S + (above ? (ptrdiff_t)(y - 1) * pt : 0);
+        const int64_t *qt = tb.Q + (above ? (ptrdiff_t)(y - 1) * pt : 0);
+        for (int i = threadIdx.x; i <= a.W; i += ROW_T) {
+            const int x = i - 1;
+            uint32_t vs = 0, vq = 0;
+            if (tb.tx + x >= 0) {
+                vs = (uint32_t)(sb[x] - (above ? st[x] : 0));
+                vq = (uint32_t)(qb[x] - (above ? qt[x] : 0));
+            }
+            cS[i] = vs;
+            cQ[i] = vq;
         }
     }
     __syncthreads();
@@ -363,8 +372,8 @@ __global__ __launch_bounds__(ROW_T) void fft_rows_c2r_coef(const double2 *__rest
         const int x = threadIdx.x + i * ROW_T;
         if (x >= a.Wo) break;
         const long long sumIT = sit[i];
-        const long long sumI = (long long)(cS[x + a.wT - 1] - (x > 0 ? cS[x - 1] : 0u));
-        const long long sumISq = (long long)(cQ[x + a.wT - 1] - (x > 0 ? cQ[x - 1] : 0u));
+        const long long sumI = (long long)(cS[x + a.wT] - cS[x]);
+        const long long sumISq = (long long)(cQ[x + a.wT] - cQ[x]);
         const long long num = K * sumIT - sumI * ts.sumT;
         const long long varI = K * sumISq - sumI * sumI;
         const size_t o = o_row + x;
@@ -421,8 +430,7 @@ size_t corr_fft_bytes(int W, int H) {
     return 3 * spec + (size_t)TWN * sizeof(double2) + 3 * 256;
 }
 
-hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q, void *work,
-                           hipStream_t st) {
+hipError_t corr_fft_launch(const CorrArgs &a, const Tables &tb, void *work, hipStream_t st) {
     FftGeom g;
     if (!fft_geometry(a.W, a.H, &g)) return hipErrorNotSupported;
     static bool attr_set[NCC_MAX_DEVICES] = {};
@@ -445,7 +453,7 @@ hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q
     double2 *tw = (double2 *)(base + 3 * spec);
     const int M = 1 << g.eM, P = 1 << g.eP, P1 = 1 << g.eP1, P2 = 1 << g.eP2;
     const size_t rowLds = (size_t)(M + M / 2) * sizeof(double2);
-    const size_t c2rLds = rowLds;  // cS, cQ (8 W <= 16 M bytes) reuse the samples
+    const size_t c2rLds = rowLds;  // cS, cQ (8 (W + 1) <= 24 M bytes) reuse it
     const size_t c1Lds = (size_t)P1 * FFT_TB * sizeof(double2);
     const size_t c2Lds = (size_t)P2 * FFT_TB * sizeof(double2);
     const dim3 blk(FFT_T);
@@ -475,7 +483,7 @@ hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q
         hipLaunchKernelGGL(fft_cols_pass1<true>, dim3(g.tiles, P2), blk, c1Lds, st, wspec, g.pitch,
                            g.eP1, g.eP2, P, a.Ho, (const double2 *)tw);
         hipLaunchKernelGGL(fft_rows_c2r_coef, dim3(a.Ho), dim3(ROW_T), c2rLds, st, (const double2 *)wspec,
-                           g.pitch, g.eM, scale, a, t, S, Q, (const double2 *)tw);
+                           g.pitch, g.eM, scale, a, t, tb, (const double2 *)tw);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

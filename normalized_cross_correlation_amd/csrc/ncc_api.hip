@@ -1,128 +1,160 @@
 // C ABI of libncc.so (declared in include/ncc.h): argument validation,
-// the per-device, per-stream workspace cache, and dispatch to the kernels.
+// options, the per-device, per-stream workspace cache, and dispatch to the
+// kernels.
 #include "ncc.h"
 #include "ncc_internal.h"
 
+#include <atomic>
 #include <climits>
-#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
+
+namespace ncc {
+
+namespace {
+// Process-wide options, indexed by NCC_OPT_*.
+std::atomic<int> g_opt[7] = {0, NCC_ROUTE_AUTO, NCC_SAT_TWO_PASS, 0, 0, 1 << 22, 0};
+}  // namespace
+
+int opt_get(int option) {
+    return option >= 1 && option <= 6 ? g_opt[option].load(std::memory_order_relaxed) : 0;
+}
+
+}  // namespace ncc
 
 namespace {
 
 using namespace ncc;
 
-struct Work {
+struct Block {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
 
-std::mutex g_mu;
-std::map<std::pair<int, hipStream_t>, Work> g_work;
+// What the library keeps for one (device, stream): the workspace, the
+// single-pass build state with its pinned failure word, and the blocks that
+// calls have outgrown.  Outgrown blocks are not freed before ncc_release: a
+// HIP graph captured earlier on the stream may still replay kernels that use
+// them.
+struct StreamRec {
+    Block work;
+    Block state;
+    uint32_t *hostflag = nullptr;  // pinned host word (host address)
+    uint32_t *devflag = nullptr;   // its device address
+    std::vector<void *> retired;
+};
 
-// A workspace of at least `bytes` for (current device, stream).  Growing
-// waits for the stream so that kernels still reading the old block finish
-// first; that is not allowed under stream capture, which gets
-// NCC_EUNSUPPORTED (call once outside the capture to size the workspace).
-int get_work(hipStream_t st, size_t bytes, void **out) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return NCC_EHIP;
-    std::lock_guard<std::mutex> lock(g_mu);
-    Work &w = g_work[std::make_pair(dev, st)];
-    if (w.bytes >= bytes && w.ptr) {
-        *out = w.ptr;
-        return NCC_OK;
-    }
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, StreamRec> g_rec;
+
+int capturing(hipStream_t st, bool *yes) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) != hipSuccess) return NCC_EHIP;
-    if (cs != hipStreamCaptureStatusNone) return NCC_EUNSUPPORTED;
-    if (w.ptr) {
-        if (hipStreamSynchronize(st) != hipSuccess) return NCC_EHIP;
-        if (hipFree(w.ptr) != hipSuccess) return NCC_EHIP;
-        w.ptr = nullptr;
-        w.bytes = 0;
-    }
-    size_t want = bytes + bytes / 4;  // headroom against repeated small growth
-    if (hipMalloc(&w.ptr, want) != hipSuccess) {
+    *yes = cs != hipStreamCaptureStatusNone;
+    return NCC_OK;
+}
+
+// The record of (current device, st); the caller holds g_mu.
+int rec_of(hipStream_t st, StreamRec **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return NCC_EHIP;
+    *out = &g_rec[std::make_pair(dev, st)];
+    return NCC_OK;
+}
+
+// A block of at least `bytes` in b (grown by a quarter beyond the request
+// against repeated small growth); a zero-filled one when `zero`.  Growing is
+// refused during stream capture (NCC_EUNSUPPORTED: call once outside the
+// capture to size the stream's blocks).  The caller holds g_mu.
+int grow(StreamRec &r, Block &b, size_t bytes, bool zero, hipStream_t st) {
+    if (b.ptr && b.bytes >= bytes) return NCC_OK;
+    bool cap = false;
+    int rc = capturing(st, &cap);
+    if (rc != NCC_OK) return rc;
+    if (cap) return NCC_EUNSUPPORTED;
+    size_t want = zero ? bytes : bytes + bytes / 4;
+    void *p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) {
         (void)hipGetLastError();
-        w.ptr = nullptr;
-        if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
+        want = bytes;
+        if (hipMalloc(&p, want) != hipSuccess) {
             (void)hipGetLastError();
-            w.ptr = nullptr;
             return NCC_ENOMEM;
         }
-        want = bytes;
     }
-    w.bytes = want;
-    *out = w.ptr;
-    return NCC_OK;
-}
-
-// State of the single-pass table build for (current device, stream): kept
-// between calls and zero-filled when (re)allocated.  Same growth rules as
-// the workspace.
-std::map<std::pair<int, hipStream_t>, Work> g_state;
-
-int get_state(hipStream_t st, size_t bytes, void **out, size_t *have) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return NCC_EHIP;
-    std::lock_guard<std::mutex> lock(g_mu);
-    Work &w = g_state[std::make_pair(dev, st)];
-    if (w.bytes >= bytes && w.ptr) {
-        *out = w.ptr;
-        *have = w.bytes;
-        return NCC_OK;
-    }
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return NCC_EHIP;
-    if (cs != hipStreamCaptureStatusNone) return NCC_EUNSUPPORTED;
-    if (w.ptr) {
-        if (hipStreamSynchronize(st) != hipSuccess) return NCC_EHIP;
-        if (hipFree(w.ptr) != hipSuccess) return NCC_EHIP;
-        w.ptr = nullptr;
-        w.bytes = 0;
-    }
-    if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        w.ptr = nullptr;
-        return NCC_ENOMEM;
-    }
-    if (hipMemsetAsync(w.ptr, 0, bytes, st) != hipSuccess) {
-        (void)hipFree(w.ptr);
-        w.ptr = nullptr;
+    if (zero && hipMemsetAsync(p, 0, want, st) != hipSuccess) {
+        (void)hipFree(p);
         return NCC_EHIP;
     }
-    w.bytes = bytes;
-    *out = w.ptr;
-    *have = bytes;
+    if (b.ptr) r.retired.push_back(b.ptr);
+    b.ptr = p;
+    b.bytes = want;
     return NCC_OK;
 }
 
-// Table build route: NCC_SAT_PATH = "fused" (single pass) or "passes".
-bool sat_fused_from_env() {
-    const char *e = std::getenv("NCC_SAT_PATH");
-    return e && !std::strcmp(e, "fused");
+int get_work(hipStream_t st, size_t bytes, void **out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    StreamRec *r = nullptr;
+    int rc = rec_of(st, &r);
+    if (rc != NCC_OK) return rc;
+    rc = grow(*r, r->work, bytes, false, st);
+    if (rc == NCC_OK) *out = r->work.ptr;
+    return rc;
 }
 
-// Builds S and Q of the H x W image with row pitch ip on `st`, with `wk`
-// (three-pass scratch) carved by the caller.
-int build_tables(const uint8_t *img, int W, int H, size_t ip, int64_t *S, int64_t *Q,
-                 const SatWork &wk, hipStream_t st) {
-    SatState fs{nullptr, nullptr, 0};
-    if (sat_fused_from_env()) {
-        void *p = nullptr;
-        size_t have = 0;
-        int rc = get_state(st, sat_state_bytes(W, H), &p, &have);
+// A reported single-pass failure: waits for the stream, zero-fills its build
+// state and clears the word.  Not possible during capture (the failure stays
+// pending).  The caller holds g_mu.
+int take_failure(StreamRec &r, hipStream_t st) {
+    if (!r.hostflag || __atomic_load_n(r.hostflag, __ATOMIC_ACQUIRE) == 0) return NCC_OK;
+    bool cap = false;
+    if (capturing(st, &cap) != NCC_OK || cap) return NCC_EHIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return NCC_EHIP;
+    if (r.state.ptr && (hipMemsetAsync(r.state.ptr, 0, r.state.bytes, st) != hipSuccess ||
+                        hipStreamSynchronize(st) != hipSuccess))
+        return NCC_EHIP;
+    __atomic_store_n(r.hostflag, 0u, __ATOMIC_RELEASE);
+    return NCC_EHIP;
+}
+
+// The single-pass build state of (current device, st): at least `bytes`,
+// zero-filled when (re)allocated, with the pinned failure word.  Reports (and
+// clears) a failure of an earlier single-pass build on the stream.
+int get_state(hipStream_t st, size_t bytes, SatState *fs) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    StreamRec *r = nullptr;
+    int rc = rec_of(st, &r);
+    if (rc != NCC_OK) return rc;
+    rc = take_failure(*r, st);
+    if (rc != NCC_OK) return rc;
+    if (!r->hostflag) {
+        bool cap = false;
+        rc = capturing(st, &cap);
         if (rc != NCC_OK) return rc;
-        fs = sat_state_view(p, have);
+        if (cap) return NCC_EUNSUPPORTED;
+        void *h = nullptr, *d = nullptr;
+        if (hipHostMalloc(&h, 256, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
+            (void)hipGetLastError();
+            return NCC_ENOMEM;
+        }
+        if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess) {
+            (void)hipHostFree(h);
+            return NCC_EHIP;
+        }
+        std::memset(h, 0, 256);
+        r->hostflag = (uint32_t *)h;
+        r->devflag = (uint32_t *)d;
     }
-    hipError_t e = sat_build_launch(img, W, H, ip, S, Q, wk, fs, st);
-    return e == hipSuccess ? NCC_OK : (e == hipErrorNotSupported ? NCC_EUNSUPPORTED : NCC_EHIP);
+    rc = grow(*r, r->state, bytes, true, st);
+    if (rc != NCC_OK) return rc;
+    *fs = sat_state_view(r->state.ptr, r->state.bytes);
+    fs->hostflag = r->devflag;
+    fs->spin = opt_get(NCC_OPT_SAT_SPIN);
+    return NCC_OK;
 }
-
-size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return NCC_OK;
@@ -130,21 +162,25 @@ int hip_status(hipError_t e) {
     return NCC_EHIP;
 }
 
-// Which correlation route to take; NCC_CORR_PATH selects one explicitly
-// ("generic", "fft", "single" for one template at a time, "dot4" for the
-// vector-unit streaming kernel, "tile" for the vector-unit tile kernel,
-// default "auto").
-enum class Route { Auto, Generic, Fft, Single, Dot4, Tile };
-Route route_from_env() {
-    const char *e = std::getenv("NCC_CORR_PATH");
-    if (!e) return Route::Auto;
-    if (!std::strcmp(e, "generic")) return Route::Generic;
-    if (!std::strcmp(e, "fft")) return Route::Fft;
-    if (!std::strcmp(e, "single")) return Route::Single;
-    if (!std::strcmp(e, "dot4")) return Route::Dot4;
-    if (!std::strcmp(e, "tile")) return Route::Tile;
-    return Route::Auto;
+// Builds S and Q of the H x W image with row pitch ip on `st`, with `wk`
+// (two-pass scratch) carved by the caller; the single-pass build when the
+// option selects it.
+int build_tables(const uint8_t *img, int W, int H, size_t ip, int64_t *S, int64_t *Q,
+                 const SatWork &wk, hipStream_t st) {
+    SatState fs{nullptr, nullptr, 0, nullptr, 0};
+    if (opt_get(NCC_OPT_SAT_BUILD) == NCC_SAT_SINGLE_PASS) {
+        int rc = get_state(st, sat_state_bytes(W, H), &fs);
+        if (rc != NCC_OK) return rc;
+        int stale = 1;
+        if (g_opt[NCC_OPT_SAT_STALE].compare_exchange_strong(stale, 0)) {
+            rc = hip_status(sat_state_poison_launch(fs, st));
+            if (rc != NCC_OK) return rc;
+        }
+    }
+    return hip_status(sat_build_launch(img, W, H, ip, S, Q, wk, fs, st));
 }
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Whether a template that no specialised kernel takes goes through the FFT
 // numerator rather than the direct generic kernel: estimated times from the
@@ -152,10 +188,10 @@ Route route_from_env() {
 // templates; FFT: ~10 spectrum passes per template and 3 for the image, each
 // pass moving the spectrum twice at ~5.3 TB/s).  At 4096 x 4096 the two
 // meet near a 48 x 48 template (0.73 ms each).
-bool fft_chosen(Route route, int Wv, int Hv, int Wo, int Ho, int wT, int hT, int nTpl) {
+bool fft_chosen(int route, int Wv, int Hv, int Wo, int Ho, int wT, int hT, int nTpl) {
     if (!corr_fft_supported(Wv, Hv)) return false;
-    if (route == Route::Fft) return true;
-    if (route != Route::Auto) return false;
+    if (route == NCC_ROUTE_FFT) return true;
+    if (route != NCC_ROUTE_AUTO) return false;
     const double spec = (double)corr_fft_bytes(Wv, Hv) / 3.0;
     const double t_fft = 20e-6 + (3.0 + 10.0 * nTpl) * 2.0 * spec / 5.3e12;
     const double t_direct = (double)nTpl * Wo * (double)Ho * wT * (double)hT / 55e12;
@@ -164,7 +200,8 @@ bool fft_chosen(Route route, int Wv, int Hv, int Wo, int Ho, int wT, int hT, int
 
 // One correlation: positions x0 <= x < x0 + w, y0 <= y < y0 + h of the H x W
 // image at img (row pitch ip bytes); output planes of h rows with pitch op
-// elements.  Arguments are validated by the caller; w, h >= 1.
+// elements; S, Q the caller's tables of the whole image (pitch W) or null.
+// Arguments are validated by the caller; w, h >= 1.
 struct Request {
     const uint8_t *img;
     int W, H;
@@ -175,27 +212,30 @@ struct Request {
     size_t op;
     int32_t *sums;
     float *coef;
+    const int64_t *S, *Q;
 };
 
 int correlate_request(const Request &r, hipStream_t st) {
     const int wT = r.wT, hT = r.hT, nTpl = r.nTpl;
-    const Route route = route_from_env();
-    const bool bank = route == Route::Auto && corr_bank_supported(wT, hT, nTpl);
+    const int route = opt_get(NCC_OPT_CORR_ROUTE);
+    const bool autor = route == NCC_ROUTE_AUTO;
+    const bool bank = autor && corr_bank_supported(wT, hT, nTpl);
     // single-template kernels: the matrix-core one, else the dot4 stream
-    const bool single_route = route == Route::Auto || route == Route::Single;
+    const bool single_route = autor || route == NCC_ROUTE_SINGLE;
     // (small launches, e.g. a local search, take the vector-unit kernel;
-    // NCC_CORR_PATH=single forces the matrix-core one where it applies)
+    // NCC_ROUTE_SINGLE forces the matrix-core one where it applies)
     const bool toep_ok = single_route && corr_toeplitz_supported(wT, hT) &&
-                         (route == Route::Single || corr_toeplitz_preferred(r.w, r.h));
-    const bool stream_ok = toep_ok || ((single_route || route == Route::Dot4) &&
+                         (route == NCC_ROUTE_SINGLE || corr_toeplitz_preferred(r.w, r.h));
+    const bool stream_ok = toep_ok || ((single_route || route == NCC_ROUTE_DOT4) &&
                                        corr_stream_supported(wT, hT));
     // the tile kernel: templates up to 32 x 64 that no kernel above takes
-    const bool tile_ok = !bank && !stream_ok && (route == Route::Auto || route == Route::Tile) &&
+    const bool tile_ok = !bank && !stream_ok && (autor || route == NCC_ROUTE_TILE) &&
                          corr_tile_supported(wT, hT);
     const bool need_tables = !bank && !stream_ok && !tile_ok;  // the generic and FFT routes
     if (need_tables && !corr_generic_supported(wT, hT)) return NCC_EUNSUPPORTED;
     const bool fft = need_tables && fft_chosen(route, r.w + wT - 1, r.h + hT - 1, r.w, r.h, wT,
                                                hT, nTpl);
+    const bool own_tables = need_tables && !r.S;  // tables built here, of the view
 
     // The view the kernels see: the rows and columns the positions' windows
     // cover.  For the streaming kernel on an image with 16-byte aligned rows,
@@ -238,17 +278,18 @@ int correlate_request(const Request &r, hipStream_t st) {
         return NCC_OK;
     }
 
-    // workspace: packed templates, per-template constants, and (generic
-    // route only) the tables of the view and their build scratch
+    // workspace: packed templates, per-template constants, and (table routes
+    // without caller tables) the tables of the view and their build scratch,
+    // and (FFT) the spectra
     const int W = a.W, H = a.H;
     size_t off_rows = 0;
     size_t off_mfma = round256(off_rows + tpl_rows_bytes(wT, hT, nTpl));
     size_t off_stats = round256(off_mfma + (bank ? tpl_mfma_bytes(wT, hT, nTpl) : 0));
     size_t off_S = round256(off_stats + sizeof(TStat) * (size_t)nTpl);
-    size_t tbl = need_tables ? (size_t)W * H * sizeof(int64_t) : 0;
+    size_t tbl = own_tables ? (size_t)W * H * sizeof(int64_t) : 0;
     size_t off_Q = round256(off_S + tbl);
     size_t off_sat = round256(off_Q + tbl);
-    size_t off_fft = round256(off_sat + (need_tables ? sat_work_bytes(W, H) : 0));
+    size_t off_fft = round256(off_sat + (own_tables ? sat_work_bytes(W, H) : 0));
     size_t total = off_fft + (fft ? corr_fft_bytes(W, H) : 0);
 
     void *ws = nullptr;
@@ -266,18 +307,21 @@ int correlate_request(const Request &r, hipStream_t st) {
 
     if (bank) return hip_status(corr_bank_launch(a, st));
 
-    const int64_t *S = nullptr, *Q = nullptr;
-    if (need_tables) {
+    Tables tb;
+    if (own_tables) {
         int64_t *Sm = (int64_t *)(base + off_S), *Qm = (int64_t *)(base + off_Q);
         SatWork wk = sat_work_carve(base + off_sat, W, H);
         rc = build_tables(a.img, W, H, a.ip, Sm, Qm, wk, st);
         if (rc != NCC_OK) return rc;
-        S = Sm;
-        Q = Qm;
+        tb = Tables{Sm, Qm, (size_t)W, 0, 0};
+    } else {
+        // the caller's tables of the whole image: the view starts at (x0, y0)
+        const size_t o = (size_t)r.y0 * (size_t)r.W + (size_t)r.x0;
+        tb = Tables{r.S + o, r.Q + o, (size_t)r.W, r.x0, r.y0};
     }
-    if (fft) return hip_status(corr_fft_launch(a, S, Q, base + off_fft, st));
+    if (fft) return hip_status(corr_fft_launch(a, tb, base + off_fft, st));
     for (int t = 0; t < nTpl; t++) {
-        e = corr_generic_launch(a, t, S, Q, st);
+        e = corr_generic_launch(a, t, tb, st);
         if (e != hipSuccess) return hip_status(e);
     }
     return NCC_OK;
@@ -287,7 +331,7 @@ int correlate_request(const Request &r, hipStream_t st) {
 
 extern "C" {
 
-int ncc_version(void) { return 101; }
+int ncc_version(void) { return 200; }
 
 const char *ncc_strerror(int status) {
     switch (status) {
@@ -299,6 +343,38 @@ const char *ncc_strerror(int status) {
         case NCC_EUNSUPPORTED: return "shape not supported by this build";
         default: return "unknown status";
     }
+}
+
+int ncc_set_option(int option, int value) {
+    bool ok = false;
+    switch (option) {
+        case NCC_OPT_CORR_ROUTE: ok = value >= NCC_ROUTE_AUTO && value <= NCC_ROUTE_TILE; break;
+        case NCC_OPT_SAT_BUILD: ok = value == NCC_SAT_TWO_PASS || value == NCC_SAT_SINGLE_PASS; break;
+        case NCC_OPT_TZ_STRIP: ok = value == 0 || value == 16 || value == 32; break;
+        case NCC_OPT_STREAM_ROWS: ok = value == 0 || value == 16 || value == 32 || value == 64; break;
+        case NCC_OPT_SAT_SPIN: ok = value >= 0; break;
+        case NCC_OPT_SAT_STALE: ok = value == 0 || value == 1; break;
+        default: break;
+    }
+    if (!ok) return NCC_EINVAL;
+    g_opt[option].store(value, std::memory_order_relaxed);
+    return NCC_OK;
+}
+
+int ncc_get_option(int option, int *value) {
+    if (!value || option < 1 || option > 6) return NCC_EINVAL;
+    *value = g_opt[option].load(std::memory_order_relaxed);
+    return NCC_OK;
+}
+
+int ncc_stream_status(void *stream) {
+    hipStream_t st = (hipStream_t)stream;
+    if (hipStreamSynchronize(st) != hipSuccess) return NCC_EHIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    StreamRec *r = nullptr;
+    int rc = rec_of(st, &r);
+    if (rc != NCC_OK) return rc;
+    return take_failure(*r, st);
 }
 
 int ncc_sat_build(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q, void *stream) {
@@ -324,8 +400,10 @@ int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n, int
 }
 
 int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl, int wT, int hT,
-                  int nTpl, int32_t *sums_out, float *coef_out, void *stream) {
+                  int nTpl, int32_t *sums_out, float *coef_out, const int64_t *S,
+                  const int64_t *Q, void *stream) {
     if (!img || !tpl || !coef_out) return NCC_EINVAL;
+    if (!S != !Q) return NCC_EINVAL;
     if (W < 1 || H < 1 || wT < 1 || hT < 1 || nTpl < 1 || wT > W || hT > H) return NCC_EINVAL;
     if (W > NCC_MAX_WIDTH) return NCC_ERANGE;
     if ((long long)wT * hT > NCC_MAX_TEMPLATE_PIXELS) return NCC_ERANGE;
@@ -350,13 +428,17 @@ int ncc_correlate(const uint8_t *img, int W, int H, const uint8_t *tpl, int wT, 
     r.op = (size_t)Wo;
     r.sums = sums_out;
     r.coef = coef_out;
+    r.S = S;
+    r.Q = Q;
     return correlate_request(r, (hipStream_t)stream);
 }
 
 int ncc_correlate_rect(const uint8_t *img, int W, int H, size_t img_pitch, const uint8_t *tpl,
                        int wT, int hT, int nTpl, int x0, int y0, int w, int h,
-                       size_t out_pitch, int32_t *sums_out, float *coef_out, void *stream) {
+                       size_t out_pitch, int32_t *sums_out, float *coef_out, const int64_t *S,
+                       const int64_t *Q, void *stream) {
     if (!img || !tpl) return NCC_EINVAL;
+    if (!S != !Q) return NCC_EINVAL;
     if (W < 1 || H < 1 || wT < 1 || hT < 1 || nTpl < 1 || wT > W || hT > H) return NCC_EINVAL;
     if (img_pitch < (size_t)W || w < 0 || h < 0 || out_pitch < (size_t)w) return NCC_EINVAL;
     if ((long long)wT * hT > NCC_MAX_TEMPLATE_PIXELS) return NCC_ERANGE;
@@ -368,6 +450,9 @@ int ncc_correlate_rect(const uint8_t *img, int W, int H, size_t img_pitch, const
     // its table corners stay inside int64
     if ((long long)w + wT - 1 > NCC_MAX_WIDTH) return NCC_ERANGE;
     if ((unsigned long long)(w + wT - 1) * (unsigned long long)(h + hT - 1) > (1ull << 40))
+        return NCC_ERANGE;
+    // caller tables cover the whole image: the same bounds as ncc_sat_build's
+    if (S && (W > NCC_MAX_WIDTH || (unsigned long long)W * (unsigned long long)H > (1ull << 40)))
         return NCC_ERANGE;
     if (out_pitch > NCC_MAX_OUT_PITCH) return NCC_ERANGE;
     const unsigned long long planes = (unsigned long long)nTpl + 2;
@@ -391,6 +476,8 @@ int ncc_correlate_rect(const uint8_t *img, int W, int H, size_t img_pitch, const
     r.op = out_pitch;
     r.sums = sums_out;
     r.coef = coef_out;
+    r.S = S;
+    r.Q = Q;
     return correlate_request(r, (hipStream_t)stream);
 }
 
@@ -398,22 +485,16 @@ void ncc_release(void) {
     std::lock_guard<std::mutex> lock(g_mu);
     int cur = 0;
     (void)hipGetDevice(&cur);
-    for (auto &kv : g_work) {
-        if (!kv.second.ptr) continue;
-        if (hipSetDevice(kv.first.first) == hipSuccess) {
-            (void)hipDeviceSynchronize();
-            (void)hipFree(kv.second.ptr);
-        }
+    for (auto &kv : g_rec) {
+        StreamRec &r = kv.second;
+        if (hipSetDevice(kv.first.first) != hipSuccess) continue;
+        (void)hipDeviceSynchronize();
+        if (r.work.ptr) (void)hipFree(r.work.ptr);
+        if (r.state.ptr) (void)hipFree(r.state.ptr);
+        for (void *p : r.retired) (void)hipFree(p);
+        if (r.hostflag) (void)hipHostFree(r.hostflag);
     }
-    g_work.clear();
-    for (auto &kv : g_state) {
-        if (!kv.second.ptr) continue;
-        if (hipSetDevice(kv.first.first) == hipSuccess) {
-            (void)hipDeviceSynchronize();
-            (void)hipFree(kv.second.ptr);
-        }
-    }
-    g_state.clear();
+    g_rec.clear();
     (void)hipSetDevice(cur);
 }
 

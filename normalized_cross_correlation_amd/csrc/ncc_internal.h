@@ -6,7 +6,12 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "ncc.h"
+
 namespace ncc {
+
+// Current value of a process-wide option (NCC_OPT_* of ncc.h).
+int opt_get(int option);
 
 // ---------------------------------------------------------------- tables ---
 // Table build tiling: tiles of SAT_SW columns x SAT_TR rows (strip s, tile
@@ -26,15 +31,20 @@ struct SatWork {
 };
 
 // State of the single-pass build, kept per (device, stream) between calls:
-// ctl = {next tile ticket, finished tiles, call epoch, spin-limit flag} and
-// two parity buffers of published tile words ([2][capTiles][SAT_FWORDS]
-// uint64).  A call works in buffer epoch & 1 and clears the other one for
-// the next call; the last tile to finish resets the counters and advances
-// the epoch.  Zero-filled when allocated.
+// ctl = {next tile ticket, finished tiles, call epoch, failure flag} and two
+// parity buffers of published tile words ([2][capTiles][SAT_FWORDS] uint64).
+// A call works in buffer epoch & 1 and clears the other one for the next
+// call; the last tile to finish resets the counters and advances the epoch.
+// Zero-filled when allocated and after a reported failure.  A workgroup whose
+// bounded wait gives up, or that draws a ticket past the last tile, also
+// stores 1 into *hostflag (pinned host memory, read by the host at the
+// stream's next single-pass build and by ncc_stream_status).
 struct SatState {
     uint32_t *ctl;
     uint64_t *words;
     int capTiles;
+    uint32_t *hostflag;  // device address of the pinned host word
+    int spin;            // polls of a wait before it gives up
 };
 constexpr int SAT_FW = 128;          // single-pass tile: columns
 constexpr int SAT_FSUB = 4;          // ... bands of SAT_BH rows
@@ -44,6 +54,9 @@ SatState sat_state_view(void *base, size_t bytes);
 
 size_t sat_work_bytes(int W, int H);
 SatWork sat_work_carve(void *base, int W, int H);
+// Sets the state's ticket counter past the last tile (the state a call that
+// never finished would leave): the failure path of ncc_stream_status' tests.
+hipError_t sat_state_poison_launch(const SatState &fs, hipStream_t st);
 // Tables of the H x W image whose row y starts at img + y * ip (ip >= W).
 // fs.ctl == nullptr: the three-pass build; else the single-pass build
 hipError_t sat_build_launch(const uint8_t *img, int W, int H, size_t ip, int64_t *S,
@@ -116,19 +129,27 @@ hipError_t corr_toeplitz_launch(const CorrArgs &a, int t, hipStream_t st);
 bool corr_tile_supported(int wT, int hT);
 hipError_t corr_tile_launch(const CorrArgs &a, int t, hipStream_t st);
 
-// Any shape: window sums from the full int64 tables S, Q.
+// Summed-area tables as the generic and FFT routes read them: view position
+// (x, y) is table element (tx + x, ty + y), S and Q point at element
+// (tx, ty), rows are `pitch` elements apart, and corners left of column 0 or
+// above row 0 of the table read as zero.
+struct Tables {
+    const int64_t *S, *Q;
+    size_t pitch;
+    int tx, ty;
+};
+
+// Any shape: window sums from the full int64 tables.
 bool corr_generic_supported(int wT, int hT);
-hipError_t corr_generic_launch(const CorrArgs &a, int t, const int64_t *S,
-                               const int64_t *Q, hipStream_t st);
+hipError_t corr_generic_launch(const CorrArgs &a, int t, const Tables &tb, hipStream_t st);
 
 // SumIT by 2-D FFT in double precision (large templates), SumI and SumISq
-// from the full int64 tables S, Q of the view.  Supported while the view's
-// padded transform sizes stay within 8192 x 8192; needs corr_fft_bytes(W, H)
-// of workspace (the spectra and the twiddle table).
+// from the full int64 tables.  Supported while the view's padded transform
+// sizes stay within 8192 x 8192; needs corr_fft_bytes(W, H) of workspace (the
+// spectra and the twiddle table).
 bool corr_fft_supported(int W, int H);
 size_t corr_fft_bytes(int W, int H);
-hipError_t corr_fft_launch(const CorrArgs &a, const int64_t *S, const int64_t *Q, void *work,
-                           hipStream_t st);
+hipError_t corr_fft_launch(const CorrArgs &a, const Tables &tb, void *work, hipStream_t st);
 
 // Template bank on the int8 matrix cores.
 bool corr_bank_supported(int wT, int hT, int nTpl);

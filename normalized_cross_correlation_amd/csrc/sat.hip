@@ -458,13 +458,22 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
 //                                  row running sum at x (from the image's
 //                                  left edge), 2 = the table value on the
 //                                  tile's last row
+//   state 3 (either kind):         the value rests on a wait that gave up;
+//                                  every tile that reads it fails as well
 // A tile waits only for words of tiles with smaller tickets, whose
 // workgroups are already running: the row words of state 1 are published
 // right after a tile's loads, the column words of state 1 after its row
 // look-back, which itself waits only for state-1 row words.  Each wait gives
-// up after SAT_FSPIN polls and raises ctl[3].
-constexpr int SAT_FSPIN = 1 << 22;
+// up after fs.spin polls; a workgroup that gave up writes INT64_MIN for its
+// tile and reports the failure (ctl[3] and the pinned host word).
 constexpr int SAT_FBATCH = 8;
+
+// A failure of this call: kind 1 = a wait gave up, 2 = a ticket past the
+// last tile (counters left by a call that never finished).
+__device__ __forceinline__ void report_failure(const SatState &fs, uint32_t kind) {
+    __hip_atomic_store(fs.ctl + 3, kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(fs.hostflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 __device__ __forceinline__ uint64_t word_load(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -474,10 +483,14 @@ __device__ __forceinline__ void word_store(uint64_t *p, uint64_t v) {
 }
 
 // Sum of the values of the words at p - stride, p - 2*stride, ... (n of
-// them), stopping after the first one of state 2; waits for words of state 0.
+// them), stopping after the first one of state 2; waits for words of state 0
+// (at most fs.spin polls each).  `failed` is set when a wait gives up or a
+// word of state 3 (published by a tile that failed) is met: the sum is then
+// not valid.
 __device__ __forceinline__ uint64_t look_back(const uint64_t *p, size_t stride, int n,
-                                              uint32_t *ctl) {
+                                              const SatState &fs, bool &failed) {
     uint64_t acc = 0;
+    failed = false;
     for (int i0 = 0; i0 < n; i0 += SAT_FBATCH) {
         uint64_t v[SAT_FBATCH];
 #pragma unroll
@@ -489,15 +502,17 @@ __device__ __forceinline__ uint64_t look_back(const uint64_t *p, size_t stride, 
             if (!done) {
                 int spins = 0;
                 while ((v[k] & 3) == 0) {
-                    if (++spins > SAT_FSPIN) {
-                        __hip_atomic_store(ctl + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (++spins > fs.spin) {
+                        report_failure(fs, 1u);
+                        failed = true;
                         break;
                     }
                     __builtin_amdgcn_s_sleep(1);
                     v[k] = word_load(p - (size_t)(i0 + k + 1) * stride);
                 }
+                if ((v[k] & 3) == 3) failed = true;
                 acc += v[k] >> 2;
-                done = (v[k] & 3) == 2;
+                done = failed || (v[k] & 3) == 2;
             }
         }
         if (done) break;
@@ -512,6 +527,7 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
     constexpr int TR = SAT_BH * SAT_FSUB;  // tile rows
     __shared__ int sh_tile;
     __shared__ uint32_t sh_epoch;
+    __shared__ int sh_fail;  // a wait of this workgroup gave up
     __shared__ uint32_t colp[4][2][SAT_FW];  // per wavefront: pixel column sums of its rows
     __shared__ uint32_t rtS[2][TR];          // row sums inside the tile
     __shared__ uint32_t lrowS[2][TR];        // row sums left of the tile
@@ -524,12 +540,13 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
     if (tid == 0) {
         sh_tile = (int)__hip_atomic_fetch_add(fs.ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sh_epoch = __hip_atomic_load(fs.ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh_fail = 0;
     }
     __syncthreads();
     const int tile = sh_tile;
     const uint32_t epoch = sh_epoch;
     if (tile >= nTiles) {  // counters not reset by the previous call: flag it, touch nothing
-        if (tid == 0) __hip_atomic_store(fs.ctl + 3, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) report_failure(fs, 2u);
         return;
     }
     const int gi = tile / nS, j = tile % nS;
@@ -586,8 +603,10 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
     // ---- row look-back: the sum of each row left of the tile
     {
         const uint32_t rt = rtS[tb][ix];
-        const uint32_t lc = (uint32_t)look_back(my + tb * TR + ix, SAT_FWORDS, j, fs.ctl);
-        word_store(my + tb * TR + ix, (uint64_t)(lc + rt) << 2 | 2u);
+        bool rf;
+        const uint32_t lc = (uint32_t)look_back(my + tb * TR + ix, SAT_FWORDS, j, fs, rf);
+        if (rf) sh_fail = 1;
+        word_store(my + tb * TR + ix, (uint64_t)(lc + rt) << 2 | (rf ? 3u : 2u));
         lrowS[tb][ix] = lc;
         const uint64_t s = wave_incl_scan_u64((uint64_t)lc);
         if (l == 63) llS[w] = s;
@@ -598,9 +617,12 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
         const uint64_t LL = llS[2 * tb] + llS[2 * tb + 1];
         const uint64_t V = (uint64_t)csS[tb][ix] + LL;
         uint64_t *cw = my + 2 * TR + tb * SAT_FW + ix;
-        word_store(cw, V << 2 | 1u);
-        const uint64_t C = look_back(cw, (size_t)nS * SAT_FWORDS, gi, fs.ctl);
-        word_store(cw, (C + V) << 2 | 2u);
+        const bool tf = sh_fail != 0;  // V rests on row sums left of the tile that failed
+        word_store(cw, V << 2 | (tf ? 3u : 1u));
+        bool cf;
+        const uint64_t C = look_back(cw, (size_t)nS * SAT_FWORDS, gi, fs, cf);
+        if (cf) sh_fail = 1;
+        word_store(cw, (C + V) << 2 | (tf || cf ? 3u : 2u));
         topS[tb][ix] = C;
     }
     __syncthreads();
@@ -608,6 +630,7 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
     // ---- the tile's rows of S and Q, band by band (as the downsweep; the
     // bytes are read again, mostly from L2, the next band's in flight while
     // the current one is stored)
+    const bool failed = sh_fail != 0;  // this tile's carries are not valid: INT64_MIN
     uint64_t s1a = topS[0][2 * l], s1b = topS[0][2 * l + 1];
     uint64_t s2a = topS[1][2 * l], s2b = topS[1][2 * l + 1];
     typedef long long v2l __attribute__((ext_vector_type(2)));
@@ -677,17 +700,19 @@ __global__ __launch_bounds__(256) void sat_fused(const uint8_t *__restrict__ img
             t2b += R2b[r];
             int64_t *srow = S + (size_t)y * W + x;
             int64_t *qrow = Q + (size_t)y * W + x;
+            const long long o1a = failed ? INT64_MIN : (long long)t1a, o1b = failed ? INT64_MIN : (long long)t1b;
+            const long long o2a = failed ? INT64_MIN : (long long)t2a, o2b = failed ? INT64_MIN : (long long)t2b;
             if (pair) {
-                *(v2l *)srow = v2l{(long long)t1a, (long long)t1b};
-                *(v2l *)qrow = v2l{(long long)t2a, (long long)t2b};
+                *(v2l *)srow = v2l{o1a, o1b};
+                *(v2l *)qrow = v2l{o2a, o2b};
             } else {
                 if (x < W) {
-                    srow[0] = (int64_t)t1a;
-                    qrow[0] = (int64_t)t2a;
+                    srow[0] = o1a;
+                    qrow[0] = o2a;
                 }
                 if (x + 1 < W) {
-                    srow[1] = (int64_t)t1b;
-                    qrow[1] = (int64_t)t2b;
+                    srow[1] = o1b;
+                    qrow[1] = o2b;
                 }
             }
         }
@@ -746,7 +771,20 @@ SatState sat_state_view(void *base, size_t bytes) {
     fs.ctl = (uint32_t *)base;
     fs.words = (uint64_t *)((char *)base + 256);
     fs.capTiles = (int)((bytes - 256) / (2 * SAT_FWORDS * sizeof(uint64_t)));
+    fs.hostflag = nullptr;
+    fs.spin = 0;
     return fs;
+}
+
+namespace {
+__global__ void sat_state_poison(uint32_t *ctl) {
+    if (threadIdx.x == 0) __hip_atomic_store(ctl, 1u << 30, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+}  // namespace
+
+hipError_t sat_state_poison_launch(const SatState &fs, hipStream_t st) {
+    hipLaunchKernelGGL(sat_state_poison, dim3(1), dim3(64), 0, st, fs.ctl);
+    return hipGetLastError();
 }
 
 hipError_t sat_build_launch(const uint8_t *img, int W, int H, size_t ip, int64_t *S, int64_t *Q,

@@ -50,7 +50,6 @@
 // instruction writes 1 KB of a row in lane order.
 #include "ncc_internal.h"
 
-#include <cstdlib>
 
 namespace ncc {
 
@@ -476,12 +475,11 @@ hipError_t launch_tz(const CorrArgs &a, int t, hipStream_t st) {
 // Strip height: 32 rows halve the halo of 16-row strips, but a launch of
 // fewer than two 32-row workgroups per CU leaves CUs idle; then 16 rows
 // (measured: 28.7 vs 30.5 us at 4096 x 4096, 19.3 vs 16.5 us for a 2048 x
-// 2048 search rectangle).  NCC_TZ_STRIP = 16 or 32 fixes it instead.
+// 2048 search rectangle).  The option NCC_OPT_TZ_STRIP = 16 or 32 fixes it
+// instead.
 int tz_strip(const CorrArgs &a) {
-    if (const char *e = std::getenv("NCC_TZ_STRIP")) {
-        const int v = std::atoi(e);
-        if (v == 16 || v == 32) return v;
-    }
+    const int v = opt_get(NCC_OPT_TZ_STRIP);
+    if (v == 16 || v == 32) return v;
     static int cus[NCC_MAX_DEVICES];
     int dev = 0, n = 256;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < NCC_MAX_DEVICES) {

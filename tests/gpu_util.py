@@ -1,5 +1,4 @@
 """Helpers for the GPU parity tests (import only from tests)."""
-import os
 import sys
 
 import numpy as np
@@ -32,20 +31,16 @@ def announce(msg):
 
 
 class route:
-    """Context manager selecting the library's correlation route."""
+    """Context manager selecting the library's correlation route (None: the
+    default choice) through ncc_set_option; restores the previous route."""
 
     def __init__(self, name):
-        self.name = name
+        self.name = name or "auto"
 
     def __enter__(self):
-        self.old = os.environ.get("NCC_CORR_PATH")
-        if self.name is None:
-            os.environ.pop("NCC_CORR_PATH", None)
-        else:
-            os.environ["NCC_CORR_PATH"] = self.name
+        import normalized_cross_correlation_amd as ncc
+        self.ctx = ncc.options(route=self.name)
+        self.ctx.__enter__()
 
     def __exit__(self, *a):
-        if self.old is None:
-            os.environ.pop("NCC_CORR_PATH", None)
-        else:
-            os.environ["NCC_CORR_PATH"] = self.old
+        self.ctx.__exit__(*a)

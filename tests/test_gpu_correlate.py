@@ -63,11 +63,11 @@ def test_single_template_routes(oracle_mod, rname, H, W, hT, wT, kind, seed):
     (143, 529, 16, 15, 53),   # ragged tail at every strip height
     (96, 256, 16, 16, 54),    # 81 rows
 ])
-def test_stream_strip_heights(oracle_mod, monkeypatch, rs, H, W, hT, wT, seed):
+def test_stream_strip_heights(oracle_mod, ncc_opts, rs, H, W, hT, wT, seed):
     """The vector-unit streaming kernel at each strip height (chosen per
     launch from the output size; fixed here)."""
     d = need_gpu()
-    monkeypatch.setenv("NCC_STREAM_RS", rs)
+    ncc_opts(stream_rows=int(rs))
     announce("correlate stream rs=%s %dx%d tpl %dx%d" % (rs, H, W, hT, wT))
     c = synth.random_case(seed, H, W, hT, wT, nTpl=1, kind="smooth")
     _compare(oracle_mod, c["img"], c["tpl"], d, route_name="dot4")
@@ -249,10 +249,10 @@ def test_errors_from_host():
     img = torch.zeros((10, 10), dtype=torch.uint8, device=d)
     out = torch.zeros((1, 1, 1), dtype=torch.float32, device=d)
     assert L.ncc_correlate(img.data_ptr(), 10, 10, img.data_ptr(), 11, 1, 1, None,
-                           out.data_ptr(), None) == -1
+                           out.data_ptr(), None, None, None) == -1
     assert L.ncc_correlate(img.data_ptr(), 70000, 1, img.data_ptr(), 1, 1, 1, None,
-                           out.data_ptr(), None) == -2
+                           out.data_ptr(), None, None, None) == -2
     assert L.ncc_correlate(img.data_ptr(), 200, 200, img.data_ptr(), 182, 182, 1, None,
-                           out.data_ptr(), None) == -2
+                           out.data_ptr(), None, None, None) == -2
     with pytest.raises(ValueError):
         ncc.correlate(img, torch.zeros((11, 2), dtype=torch.uint8, device=d))

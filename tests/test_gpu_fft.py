@@ -43,10 +43,10 @@ def test_fft_route_shapes(oracle_mod, H, W, hT, wT, n, seed):
     _compare(oracle_mod, c["img"], c["tpl"], d)
 
 
-@pytest.mark.parametrize("sat_path", ["passes", "fused"])
-def test_fft_route_both_table_builds(oracle_mod, monkeypatch, sat_path):
+@pytest.mark.parametrize("sat_path", ["two_pass", "single_pass"])
+def test_fft_route_both_table_builds(oracle_mod, ncc_opts, sat_path):
     d = need_gpu()
-    monkeypatch.setenv("NCC_SAT_PATH", sat_path)
+    ncc_opts(sat_build=sat_path)
     announce("fft route sat=%s" % sat_path)
     c = synth.random_case(21, 150, 170, 21, 13, nTpl=1, kind="smooth")
     _compare(oracle_mod, c["img"], c["tpl"], d)

@@ -21,11 +21,11 @@ def _near_white(seed, H, W):
     return img
 
 
-@pytest.mark.parametrize("sat_path", ["passes", "fused"])
-def test_sat_at_max_width(oracle_mod, monkeypatch, sat_path):
+@pytest.mark.parametrize("sat_path", ["two_pass", "single_pass"])
+def test_sat_at_max_width(oracle_mod, ncc_opts, sat_path):
     import normalized_cross_correlation_amd as ncc
     d = need_gpu()
-    monkeypatch.setenv("NCC_SAT_PATH", sat_path)
+    ncc_opts(sat_build=sat_path)
     announce("sat at max width 37x%d sat=%s" % (MAX_W, sat_path))
     img = _near_white(1, 37, MAX_W)
     S, Q = ncc.sat_build(dev(img, d))

@@ -85,12 +85,12 @@ def test_stream_rects(oracle_mod, kernel, layout, x0, y0, w, h):
 
 
 @pytest.mark.parametrize("x0,y0,w,h", [(0, 0, 5, 5), (3, 9, 57, 41), (60, 2, 71, 80)])
-@pytest.mark.parametrize("sat_path", ["passes", "fused"])
-def test_generic_rects(oracle_mod, monkeypatch, sat_path, x0, y0, w, h):
+@pytest.mark.parametrize("sat_path", ["two_pass", "single_pass"])
+def test_generic_rects(oracle_mod, ncc_opts, sat_path, x0, y0, w, h):
     """9 x 11 template: the generic kernel on the tables of the rectangle's
     view, from a pitched image."""
     d = need_gpu()
-    monkeypatch.setenv("NCC_SAT_PATH", sat_path)
+    ncc_opts(sat_build=sat_path)
     announce("rect generic sat=%s (%d,%d) %dx%d" % (sat_path, x0, y0, w, h))
     c = synth.random_case(300 + x0, 130, 145, 11, 9, nTpl=2, kind="uniform")
     iv = _strided_image(c["img"], d, 3, 9)

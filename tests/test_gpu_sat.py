@@ -2,10 +2,8 @@
 
 Tables and box sums are integers: they must match bit for bit.  Every test
 runs on both builds of the library: the three-pass build (default) and the
-single-pass look-back build (NCC_SAT_PATH=fused).
+single-pass look-back build (option sat_build = single_pass).
 """
-import os
-
 import numpy as np
 import pytest
 
@@ -15,15 +13,11 @@ from tests.gpu_util import announce, dev, host, need_gpu
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(autouse=True, params=["passes", "fused"])
+@pytest.fixture(autouse=True, params=["two_pass", "single_pass"])
 def sat_route(request):
-    old = os.environ.get("NCC_SAT_PATH")
-    os.environ["NCC_SAT_PATH"] = request.param
-    yield request.param
-    if old is None:
-        os.environ.pop("NCC_SAT_PATH", None)
-    else:
-        os.environ["NCC_SAT_PATH"] = old
+    import normalized_cross_correlation_amd as ncc
+    with ncc.options(sat_build=request.param):
+        yield request.param
 
 SHAPES = [
     # H, W: single pixel, thin, below one tile, ragged tails in both directions,
@@ -39,10 +33,10 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("H,W", SHAPES)
-def test_sat_matches_oracle(oracle_mod, H, W):
+def test_sat_matches_oracle(oracle_mod, H, W, sat_route):
     import normalized_cross_correlation_amd as ncc
     d = need_gpu()
-    announce("sat %dx%d route=%s" % (H, W, os.environ.get("NCC_SAT_PATH")))
+    announce("sat %dx%d build=%s" % (H, W, sat_route))
     rng = np.random.default_rng(H * 10007 + W)
     img = rng.integers(0, 256, (H, W), dtype=np.uint8)
     S, Q = ncc.sat_build(dev(img, d))

@@ -25,10 +25,10 @@ def _eager(ncc, img, tpl):
 
 
 @pytest.mark.parametrize("tshape,sat_path,corr_path", [
-    ((16, 16, 1), "passes", None), ((16, 16, 1), "passes", "single"),
-    ((16, 16, 20), "passes", None), ((9, 11, 1), "passes", None), ((9, 11, 1), "passes", "generic"),
-    ((16, 16, 1), "fused", None)])
-def test_graph_capture_replays(tshape, sat_path, corr_path, monkeypatch):
+    ((16, 16, 1), "two_pass", None), ((16, 16, 1), "two_pass", "single"),
+    ((16, 16, 20), "two_pass", None), ((9, 11, 1), "two_pass", None), ((9, 11, 1), "two_pass", "generic"),
+    ((16, 16, 1), "single_pass", None)])
+def test_graph_capture_replays(tshape, sat_path, corr_path, ncc_opts):
     """Table build + correlation captured once, replayed on changing images
     (the 16 x 16 single template on both of its kernels: vector units by
     default at this size, matrix cores forced; a 9 x 11 template on the tile
@@ -38,9 +38,9 @@ def test_graph_capture_replays(tshape, sat_path, corr_path, monkeypatch):
     import torch
     import normalized_cross_correlation_amd as ncc
     d = need_gpu()
-    monkeypatch.setenv("NCC_SAT_PATH", sat_path)
+    ncc_opts(sat_build=sat_path)
     if corr_path:
-        monkeypatch.setenv("NCC_CORR_PATH", corr_path)
+        ncc_opts(route=corr_path)
     hT, wT, n = tshape
     announce("graph capture tpl %dx%d n=%d sat=%s corr=%s" % (hT, wT, n, sat_path, corr_path))
     cases = [synth.random_case(60 + i, 173, 301, hT, wT, nTpl=n, kind="smooth") for i in range(3)]
@@ -104,13 +104,13 @@ def test_two_streams_concurrent():
         np.testing.assert_array_equal(host(sb), ref_b[3])
 
 
-@pytest.mark.parametrize("sat_path", ["passes", "fused"])
-def test_workspace_regrowth_between_calls(sat_path, monkeypatch):
+@pytest.mark.parametrize("sat_path", ["two_pass", "single_pass"])
+def test_workspace_regrowth_between_calls(sat_path, ncc_opts):
     """Sizes that grow and shrink on one stream reuse or regrow its workspace
     (and, for the single-pass table build, its call state)."""
     import normalized_cross_correlation_amd as ncc
     d = need_gpu()
-    monkeypatch.setenv("NCC_SAT_PATH", sat_path)
+    ncc_opts(sat_build=sat_path)
     announce("workspace regrowth sat=%s" % sat_path)
     refs = []
     shapes = [(40, 70, 16, 16, 3), (400, 900, 16, 16, 1), (33, 50, 5, 7, 2), (500, 1000, 16, 16, 64),
@@ -123,3 +123,47 @@ def test_workspace_regrowth_between_calls(sat_path, monkeypatch):
         got = _eager(ncc, dev(c["img"], d), dev(c["tpl"], d))
         for g_, r_ in zip(got, ref):
             np.testing.assert_array_equal(g_, r_)
+
+
+@pytest.mark.parametrize("sat_path", ["two_pass", "single_pass"])
+def test_graph_replay_after_workspace_growth(sat_path, ncc_opts):
+    """A graph captured on a stream, then an eager call on the same stream
+    that needs a larger workspace (and single-pass state): the block the
+    graph recorded is retired, not freed, so every later replay still matches
+    the eager results (generic route: the workspace holds the tables)."""
+    import torch
+    import normalized_cross_correlation_amd as ncc
+    d = need_gpu()
+    ncc_opts(sat_build=sat_path, route="generic")
+    announce("graph replay after workspace growth sat=%s" % sat_path)
+    small = [synth.random_case(90 + i, 150, 170, 9, 11, nTpl=2, kind="smooth") for i in range(2)]
+    large = synth.random_case(95, 900, 1300, 9, 11, nTpl=2, kind="uniform")
+    img = dev(small[0]["img"], d)
+    tpl = dev(small[0]["tpl"], d)
+    s = torch.cuda.Stream(device=d)
+    with torch.cuda.stream(s):
+        ncc.sat_build(img)
+        ncc.correlate(img, tpl, want_sums=True)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        S, Q = ncc.sat_build(img)
+        coef, sums = ncc.correlate(img, tpl, want_sums=True)
+    torch.cuda.synchronize()
+    limg, ltpl = dev(large["img"], d), dev(large["tpl"], d)
+    for rep in range(4):
+        with torch.cuda.stream(s):  # grows the stream's workspace on the first pass
+            lS, lQ = ncc.sat_build(limg)
+            lc, ls = ncc.correlate(limg, ltpl, want_sums=True)
+        torch.cuda.synchronize()
+        c = small[rep % 2]
+        img.copy_(dev(c["img"], d))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eS, eQ, ecoef, esums = _eager(ncc, img, tpl)
+        np.testing.assert_array_equal(host(S), eS)
+        np.testing.assert_array_equal(host(Q), eQ)
+        np.testing.assert_array_equal(host(sums), esums)
+        np.testing.assert_array_equal(host(coef), ecoef)
+    ncc.stream_status()

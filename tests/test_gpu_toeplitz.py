@@ -47,10 +47,10 @@ def _check(oracle_mod, img, tpl, d, want_sums=True):
 ])
 @pytest.mark.parametrize("want_sums", [True, False])
 @pytest.mark.parametrize("strip", ["16", "32"])
-def test_toeplitz_shapes(oracle_mod, monkeypatch, H, W, kind, seed, want_sums, strip):
+def test_toeplitz_shapes(oracle_mod, ncc_opts, H, W, kind, seed, want_sums, strip):
     """Both strip heights (chosen per launch from the grid size; fixed here)."""
     d = need_gpu()
-    monkeypatch.setenv("NCC_TZ_STRIP", strip)
+    ncc_opts(tz_strip=int(strip))
     announce("toeplitz %dx%d %s sums=%s strip=%s" % (H, W, kind, want_sums, strip))
     c = synth.random_case(seed, H, W, 16, 16, nTpl=1, kind=kind)
     _check(oracle_mod, c["img"], c["tpl"], d, want_sums=want_sums)

@@ -55,7 +55,7 @@ def test_header_constants_match_binding():
 
 
 def test_version_and_strerror(L):
-    assert L.ncc_version() == 101
+    assert L.ncc_version() == ncc.ABI_VERSION == 200
     for code in (0, -1, -2, -3, -4, -5):
         assert L.ncc_strerror(code)
     assert L.ncc_strerror(-99) == b"unknown status"
@@ -76,19 +76,22 @@ def test_box_rejects_and_empty(L):
 
 
 def test_correlate_rejects(L):
-    c = L.ncc_correlate
-    assert c(None, 8, 8, FAKE, 3, 3, 1, None, FAKE, None) == EINVAL
-    assert c(FAKE, 8, 8, FAKE, 9, 3, 1, None, FAKE, None) == EINVAL  # wT > W
-    assert c(FAKE, 8, 8, FAKE, 3, 3, 0, None, FAKE, None) == EINVAL
-    assert c(FAKE, 8, 8, FAKE, 3, 3, 1, None, None, None) == EINVAL
-    assert c(FAKE, ncc.MAX_WIDTH + 1, 8, FAKE, 3, 3, 1, None, FAKE, None) == ERANGE
-    assert c(FAKE, 300, 300, FAKE, 182, 182, 1, None, FAKE, None) == ERANGE  # K > 33025
+    def c(img, W, H, tpl, wT, hT, n, sums, coef, S=None, Q=None):
+        return L.ncc_correlate(img, W, H, tpl, wT, hT, n, sums, coef, S, Q, None)
+    assert c(None, 8, 8, FAKE, 3, 3, 1, None, FAKE) == EINVAL
+    assert c(FAKE, 8, 8, FAKE, 9, 3, 1, None, FAKE) == EINVAL  # wT > W
+    assert c(FAKE, 8, 8, FAKE, 3, 3, 0, None, FAKE) == EINVAL
+    assert c(FAKE, 8, 8, FAKE, 3, 3, 1, None, None) == EINVAL
+    assert c(FAKE, 8, 8, FAKE, 3, 3, 1, None, FAKE, S=FAKE) == EINVAL  # S without Q
+    assert c(FAKE, 8, 8, FAKE, 3, 3, 1, None, FAKE, Q=FAKE) == EINVAL  # Q without S
+    assert c(FAKE, ncc.MAX_WIDTH + 1, 8, FAKE, 3, 3, 1, None, FAKE) == ERANGE
+    assert c(FAKE, 300, 300, FAKE, 182, 182, 1, None, FAKE) == ERANGE  # K > 33025
 
 
 def _rect(L, W=40, H=30, ip=40, wT=5, hT=4, n=1, x0=0, y0=0, w=1, h=1, op=1, coef=FAKE,
-          img=FAKE):
+          img=FAKE, S=None, Q=None):
     return L.ncc_correlate_rect(img, W, H, ip, FAKE, wT, hT, n, x0, y0, w, h, op, None, coef,
-                                None)
+                                S, Q, None)
 
 
 def test_correlate_rect_rejects(L):
@@ -98,6 +101,8 @@ def test_correlate_rect_rejects(L):
     assert _rect(L, w=-1) == EINVAL
     assert _rect(L, w=5, op=4) == EINVAL                # output pitch below w
     assert _rect(L, coef=None) == EINVAL                # outputs needed for w, h > 0
+    assert _rect(L, S=FAKE) == EINVAL                   # S without Q
+    assert _rect(L, Q=FAKE) == EINVAL
     assert _rect(L, x0=-1) == ERANGE
     assert _rect(L, x0=Wo - 3, w=4, op=4) == ERANGE     # last window past the right edge
     assert _rect(L, y0=Ho - 2, h=3) == ERANGE
@@ -115,6 +120,58 @@ def test_correlate_rect_empty_is_noop(L):
     assert _rect(L, x0=36, w=0, op=0, coef=None) == OK  # empty at the right edge
     assert _rect(L, h=0, w=3, op=3, coef=None) == OK
     assert _rect(L, x0=40, w=0, op=0, coef=None) == ERANGE  # still validated
+
+
+def test_options(L):
+    """ncc_set_option / ncc_get_option: defaults, accepted values, rejected
+    options and values (which leave the setting unchanged)."""
+    v = ctypes.c_int()
+    defaults = {1: 0, 2: 0, 3: 0, 4: 0, 5: 1 << 22, 6: 0}
+    for opt, want in defaults.items():
+        assert L.ncc_get_option(opt, ctypes.byref(v)) == OK
+        assert v.value == want, (opt, v.value)
+    assert L.ncc_get_option(0, ctypes.byref(v)) == EINVAL
+    assert L.ncc_get_option(7, ctypes.byref(v)) == EINVAL
+    assert L.ncc_get_option(1, None) == EINVAL
+    good = {1: [0, 1, 2, 3, 4, 5], 2: [0, 1], 3: [0, 16, 32], 4: [0, 16, 32, 64], 5: [0, 7, 1 << 22],
+            6: [0, 1]}
+    bad = {1: [-1, 6], 2: [-1, 2], 3: [8, 64], 4: [8, 128], 5: [-1], 6: [2, -1]}
+    for opt in good:
+        for val in good[opt]:
+            assert L.ncc_set_option(opt, val) == OK
+            assert L.ncc_get_option(opt, ctypes.byref(v)) == OK and v.value == val
+        last = good[opt][-1]
+        for val in bad[opt]:
+            assert L.ncc_set_option(opt, val) == EINVAL
+            assert L.ncc_get_option(opt, ctypes.byref(v)) == OK and v.value == last
+        assert L.ncc_set_option(opt, defaults[opt]) == OK
+    assert L.ncc_set_option(99, 0) == EINVAL
+    # the binding's names and context manager
+    with ncc.options(route="generic", sat_build="single_pass", stream_rows=32):
+        assert ncc.get_option("route") == 1
+        assert ncc.get_option("sat_build") == 1
+        assert ncc.get_option("stream_rows") == 32
+    assert ncc.get_option("route") == 0 and ncc.get_option("sat_build") == 0
+    assert ncc.get_option("stream_rows") == 0
+    with pytest.raises(ncc.NCCError):
+        ncc.set_option("tz_strip", 24)
+    # every option and value name the header defines matches the binding
+    text = open(HEADER).read()
+    header_name = {"route": "CORR_ROUTE"}
+    for name, num in ncc.OPTIONS.items():
+        hn = header_name.get(name, name.upper())
+        assert re.search(r"#define NCC_OPT_%s %d\b" % (hn, num), text), name
+    for name, num in ncc.ROUTES.items():
+        assert re.search(r"#define NCC_ROUTE_%s %d\b" % (name.upper(), num), text), name
+
+
+def test_library_reads_no_environment():
+    """Routes are chosen by ncc_set_option only: the library's sources call
+    no getenv (a caller's environment cannot change what a call does)."""
+    csrc = os.path.join(ROOT, "normalized_cross_correlation_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, f)).read()
+        assert "getenv" not in text, f
 
 
 def test_peaks_library_exports():
