@@ -88,6 +88,28 @@ extern "C" {
 int ncc_sat_build(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q,
                   void *stream);
 
+/* Largest build scratch of ncc_sat_build_noalloc, in bytes (16 MiB): the
+ * two-pass build needs about W*H/8 bytes, so images up to about 133 million
+ * pixels (a square image up to 11520 x 11520). */
+#define NCC_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * ncc_sat_build_noalloc -- ncc_sat_build for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, tables and errors as
+ * ncc_sat_build (always its two-pass build; NCC_OPT_SAT_BUILD is not read),
+ * plus NCC_ERANGE when the image's build scratch exceeds
+ * NCC_NOALLOC_SCRATCH_BYTES.  It allocates nothing: the scratch is a fixed
+ * device array of that size, which each GPU the library runs on holds until
+ * the process ends (its address is looked up once per device, at the first
+ * call there).  Every call on a GPU shares that GPU's array, so calls that
+ * overlap on one GPU (on different streams, or a graph replayed beside other
+ * calls) race: the caller must order them.  Nothing in the array needs to
+ * start at zero.
+ */
+int ncc_sat_build_noalloc(const uint8_t *img, int W, int H, int64_t *S,
+                          int64_t *Q, void *stream);
+
 /*
  * ncc_box -- batched four-corner box sums on one table (section 15.8:
  * four-corner equation and satBox listing).
@@ -285,7 +307,7 @@ const char *ncc_strerror(int status);
  * again; HIP graphs that recorded earlier calls must be captured again. */
 void ncc_release(void);
 
-/* ABI version of this header (major*100 + minor): 200. */
+/* ABI version of this header (major*100 + minor): 201. */
 int ncc_version(void);
 
 #ifdef __cplusplus

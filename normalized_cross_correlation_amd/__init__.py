@@ -34,10 +34,10 @@ __all__ = ["sat_build", "box", "correlate", "correlate_rect", "release", "lib", 
            "ABI_FUNCTIONS", "LIB_PATH", "MAX_WIDTH", "MAX_TEMPLATE_PIXELS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libncc.so")
-ABI_FUNCTIONS = ("ncc_sat_build", "ncc_box", "ncc_correlate", "ncc_correlate_rect",
+ABI_FUNCTIONS = ("ncc_sat_build", "ncc_sat_build_noalloc", "ncc_box", "ncc_correlate", "ncc_correlate_rect",
                  "ncc_set_option", "ncc_get_option", "ncc_stream_status",
                  "ncc_strerror", "ncc_release", "ncc_version")
-ABI_VERSION = 200
+ABI_VERSION = 201
 # option numbers and values of ncc.h
 OPTIONS = {"route": 1, "sat_build": 2, "tz_strip": 3, "stream_rows": 4, "sat_spin": 5,
            "sat_stale": 6}
@@ -68,6 +68,8 @@ def lib():
         P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         L.ncc_sat_build.argtypes = [P, I, I, P, P, P]
         L.ncc_sat_build.restype = I
+        L.ncc_sat_build_noalloc.argtypes = [P, I, I, P, P, P]
+        L.ncc_sat_build_noalloc.restype = I
         L.ncc_box.argtypes = [P, I, I, P, I64, P, P]
         L.ncc_box.restype = I
         L.ncc_correlate.argtypes = [P, I, I, P, I, I, I, P, P, P, P, P]

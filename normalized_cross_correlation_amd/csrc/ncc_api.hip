@@ -25,9 +25,36 @@ int opt_get(int option) {
 
 }  // namespace ncc
 
+// ncc_sat_build_noalloc's build scratch: one fixed array per device, held
+// until the process ends and shared by every call on that device.  Host code
+// uses its device address from hipGetSymbolAddress, never the symbol itself.
+static __device__ __align__(256) unsigned char scratch[NCC_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace ncc;
+
+std::mutex g_scratch_mu;
+void *g_scratch[NCC_MAX_DEVICES];  // device address of `scratch` on each device
+
+// The address of `scratch` on the current device, looked up at the first
+// call there (with that device current).
+int scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return NCC_EHIP;
+    if (dev < 0 || dev >= NCC_MAX_DEVICES) return NCC_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return NCC_EHIP;
+        }
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return NCC_OK;
+}
 
 struct Block {
     void *ptr = nullptr;
@@ -331,7 +358,7 @@ int correlate_request(const Request &r, hipStream_t st) {
 
 extern "C" {
 
-int ncc_version(void) { return 200; }
+int ncc_version(void) { return 201; }
 
 const char *ncc_strerror(int status) {
     switch (status) {
@@ -388,6 +415,19 @@ int ncc_sat_build(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q, void
     if (rc != NCC_OK) return rc;
     SatWork wk = sat_work_carve(ws, W, H);
     return build_tables(img, W, H, (size_t)W, S, Q, wk, st);
+}
+
+int ncc_sat_build_noalloc(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q, void *stream) {
+    if (!img || !S || !Q || W < 1 || H < 1) return NCC_EINVAL;
+    if (W > NCC_MAX_WIDTH) return NCC_ERANGE;
+    if ((unsigned long long)W * (unsigned long long)H > (1ull << 40)) return NCC_ERANGE;
+    if (sat_work_bytes(W, H) > (size_t)NCC_NOALLOC_SCRATCH_BYTES) return NCC_ERANGE;
+    void *ws = nullptr;
+    int rc = scratch_address(&ws);
+    if (rc != NCC_OK) return rc;
+    const SatState none{nullptr, nullptr, 0, nullptr, 0};  // the two-pass build
+    return hip_status(sat_build_launch(img, W, H, (size_t)W, S, Q, sat_work_carve(ws, W, H), none,
+                                       (hipStream_t)stream));
 }
 
 int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n, int64_t *out,

@@ -55,7 +55,7 @@ def test_header_constants_match_binding():
 
 
 def test_version_and_strerror(L):
-    assert L.ncc_version() == ncc.ABI_VERSION == 200
+    assert L.ncc_version() == ncc.ABI_VERSION == 201
     for code in (0, -1, -2, -3, -4, -5):
         assert L.ncc_strerror(code)
     assert L.ncc_strerror(-99) == b"unknown status"
@@ -66,6 +66,16 @@ def test_sat_build_rejects(L):
     assert L.ncc_sat_build(FAKE, 0, 4, FAKE, FAKE, None) == EINVAL
     assert L.ncc_sat_build(FAKE, ncc.MAX_WIDTH + 1, 4, FAKE, FAKE, None) == ERANGE
     assert L.ncc_sat_build(FAKE, 65536, 1 << 25, FAKE, FAKE, None) == ERANGE
+
+
+def test_sat_build_noalloc_rejects(L):
+    f = L.ncc_sat_build_noalloc
+    assert f(None, 4, 4, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 4, 0, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, ncc.MAX_WIDTH + 1, 4, FAKE, FAKE, None) == ERANGE
+    # past the fixed scratch: about W*H/8 bytes against 16 MiB
+    assert f(FAKE, 16384, 16384, FAKE, FAKE, None) == ERANGE
+    assert f(FAKE, 60000, 2300, FAKE, FAKE, None) == ERANGE
 
 
 def test_box_rejects_and_empty(L):
