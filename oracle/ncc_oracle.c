@@ -10,10 +10,13 @@
  *
  * Sources (the pages this follows):
  *   [HB-SAT]  The CUDA Handbook, ch. 15, section 15.8 "The Denominator:
- *             Summed Area Tables": the table definition, the four-corner
- *             box-sum equation, the satBox listing, the width analysis
- *             (int64 table, uint32 row running sums), and the naiveRow /
- *             naiveCol listings (inclusive row scan, then column scan).
+ *             Summed Area Tables": the table definition (the sum of every
+ *             pixel above and to the left, inclusive), the four-corner
+ *             box-sum identity (Figure 15-7), and the width analysis (int64
+ *             table, uint32 row running sums).  The table and the box query
+ *             are written here from those definitions: the table by the 2-D
+ *             inclusion-exclusion recurrence over a zero border, the query
+ *             as the identity's four signed corners.
  *   [HB-SM]   The CUDA Handbook, ch. 15, "Image in shared memory": the
  *             corrShared_kernel listing, whose per-window loop accumulates
  *             SumI, SumISq and SumIT over a wTemplate x hTemplate window
@@ -64,49 +67,50 @@ void oracle_row_partials(const uint8_t *img, int W, int H,
     }
 }
 
+/* Table element (x, y), with everything left of column 0 or above row 0
+ * read as zero: the zero border that [HB-SAT] gives the table's two leading
+ * edges. */
+static int64_t tbl_at(const int64_t *T, int W, int x, int y)
+{
+    return (x < 0 || y < 0) ? 0 : T[(size_t)y * W + x];
+}
+
 /* [HB-SAT] summed-area tables S (of I) and Q (of I^2), int64, row-major with
- * pitch W: an inclusive running sum along each row, then an inclusive
- * running sum down each column.  Returns 0, or -1 on bad sizes. */
+ * pitch W, inclusive: S(x,y) is the sum of I over every pixel (x',y') with
+ * x' <= x and y' <= y.  Filled in row-major order from the identity
+ *   S(x,y) = I(x,y) + S(x-1,y) + S(x,y-1) - S(x-1,y-1)
+ * (the box [0,x] x [0,y] is its last pixel plus the box ending one column to
+ * the left plus the box ending one row up, minus the box both of those
+ * contain), with the zero border.  Returns 0, or -1 on bad sizes. */
 int oracle_sat_build(const uint8_t *img, int W, int H, int64_t *S, int64_t *Q)
 {
     if (W < 1 || H < 1 || !img || !S || !Q) return -1;
-    for (int y = 0; y < H; y++) {
-        int64_t s1 = 0, s2 = 0;
+    for (int y = 0; y < H; y++)
         for (int x = 0; x < W; x++) {
             int64_t v = img[(size_t)y * W + x];
-            s1 += v;
-            s2 += v * v;
-            S[(size_t)y * W + x] = s1;
-            Q[(size_t)y * W + x] = s2;
+            S[(size_t)y * W + x] = v + tbl_at(S, W, x - 1, y) + tbl_at(S, W, x, y - 1)
+                                   - tbl_at(S, W, x - 1, y - 1);
+            Q[(size_t)y * W + x] = v * v + tbl_at(Q, W, x - 1, y) + tbl_at(Q, W, x, y - 1)
+                                   - tbl_at(Q, W, x - 1, y - 1);
         }
-    }
-    for (int x = 0; x < W; x++) {
-        int64_t s1 = 0, s2 = 0;
-        for (int y = 0; y < H; y++) {
-            s1 += S[(size_t)y * W + x];
-            s2 += Q[(size_t)y * W + x];
-            S[(size_t)y * W + x] = s1;
-            Q[(size_t)y * W + x] = s2;
-        }
-    }
     return 0;
 }
 
-/* [HB-SAT] four-corner rule: the sum over [x0,x1) x [y0,y1) is
- * D - B - C + A with D = S(x1-1,y1-1) bottom-right, B = S(x1-1,y0-1)
- * top-right, C = S(x0-1,y1-1) bottom-left, A = S(x0-1,y0-1) top-left, and
- * the table's two leading edges read as zero.  Empty boxes sum to 0.
- * Rectangles outside the domain abort (a caller bug in a test). */
+/* [HB-SAT] four-corner identity (Figure 15-7): the sum over the half-open
+ * box [x0,x1) x [y0,y1) is the table at the box's last pixel, minus the
+ * table at the pixel above its top-right corner and at the pixel left of its
+ * bottom-left corner (each of those boxes covers one strip outside the box),
+ * plus the table at the pixel diagonally above-left of its first pixel (the
+ * part both strips removed), every corner read through the zero border.
+ * Empty boxes sum to 0.  Rectangles outside the domain abort (a caller bug
+ * in a test). */
 int64_t oracle_sat_box(const int64_t *S, int W, int H,
                        int x0, int y0, int x1, int y1)
 {
     if (x0 < 0 || y0 < 0 || x1 > W || y1 > H || x0 > x1 || y0 > y1) abort();
     if (x0 == x1 || y0 == y1) return 0;
-    int64_t D = S[(size_t)(y1 - 1) * W + (x1 - 1)];
-    int64_t B = (y0 > 0) ? S[(size_t)(y0 - 1) * W + (x1 - 1)] : 0;
-    int64_t C = (x0 > 0) ? S[(size_t)(y1 - 1) * W + (x0 - 1)] : 0;
-    int64_t A = (x0 > 0 && y0 > 0) ? S[(size_t)(y0 - 1) * W + (x0 - 1)] : 0;
-    return D - B - C + A;
+    return tbl_at(S, W, x1 - 1, y1 - 1) - tbl_at(S, W, x1 - 1, y0 - 1)
+           - tbl_at(S, W, x0 - 1, y1 - 1) + tbl_at(S, W, x0 - 1, y0 - 1);
 }
 
 /* Batch of box queries; rects holds n records {x0, y0, x1, y1}. */

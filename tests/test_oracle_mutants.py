@@ -16,14 +16,18 @@ SRC = os.path.join(ROOT, "oracle", "ncc_oracle.c")
 PINS = ["tests/test_oracle_sat.py", "tests/test_oracle_correlate.py"]
 
 MUTANTS = {
-    "box_drops_top_left": ("return D - B - C + A;", "return D - B - C;"),
-    "box_wrong_sign": ("return D - B - C + A;", "return D - B + C - A;"),
-    "box_transposed_corner": ("S[(size_t)(y0 - 1) * W + (x1 - 1)]", "S[(size_t)(x1 - 1) * W + (y0 - 1)]"),
-    "box_corner_guard": ("(x0 > 0 && y0 > 0)", "(x0 > 0)"),
-    "table_column_pass_mixes_tables": ("s2 += Q[(size_t)y * W + x];", "s2 += S[(size_t)y * W + x];"),
-    "table_row_pass_drops_square": ("            s2 += v * v;\n            S[", "            s2 += v;\n            S["),
-    "table_exclusive": ("            s1 += v;\n            s2 += v * v;\n            S[(size_t)y * W + x] = s1;\n            Q[(size_t)y * W + x] = s2;",
-                        "            S[(size_t)y * W + x] = s1;\n            Q[(size_t)y * W + x] = s2;\n            s1 += v;\n            s2 += v * v;"),
+    "box_drops_top_left": ("           - tbl_at(S, W, x0 - 1, y1 - 1) + tbl_at(S, W, x0 - 1, y0 - 1);",
+                           "           - tbl_at(S, W, x0 - 1, y1 - 1);"),
+    "box_wrong_sign": ("           - tbl_at(S, W, x0 - 1, y1 - 1) + tbl_at(S, W, x0 - 1, y0 - 1);",
+                       "           + tbl_at(S, W, x0 - 1, y1 - 1) - tbl_at(S, W, x0 - 1, y0 - 1);"),
+    "box_transposed_corner": ("- tbl_at(S, W, x1 - 1, y0 - 1)", "- tbl_at(S, W, y0 - 1, x1 - 1)"),
+    "box_corner_shifted": ("+ tbl_at(S, W, x0 - 1, y0 - 1);", "+ tbl_at(S, W, x0, y0 - 1);"),
+    "table_mixes_tables": ("Q[(size_t)y * W + x] = v * v + tbl_at(Q, W, x - 1, y) + tbl_at(Q, W, x, y - 1)",
+                           "Q[(size_t)y * W + x] = v * v + tbl_at(Q, W, x - 1, y) + tbl_at(S, W, x, y - 1)"),
+    "table_drops_square": ("Q[(size_t)y * W + x] = v * v +", "Q[(size_t)y * W + x] = v +"),
+    "table_exclusive": ("S[(size_t)y * W + x] = v + tbl_at(S, W, x - 1, y)", "S[(size_t)y * W + x] = tbl_at(S, W, x - 1, y)"),
+    "table_drops_overlap": ("                                   - tbl_at(S, W, x - 1, y - 1);\n",
+                            "                                   ;\n"),
     "numerator_sign": ("int64_t num = K * sumIT - sumI * sumT;", "int64_t num = K * sumIT + sumI * sumT;"),
     "numerator_drops_count": ("int64_t num = K * sumIT - sumI * sumT;", "int64_t num = sumIT - sumI * sumT;"),
     "window_variance_term": ("int64_t varI = K * sumISq - sumI * sumI;", "int64_t varI = K * sumISq - sumI;"),

@@ -2,11 +2,11 @@
 
 What pins what (The CUDA Handbook ch. 15, section 15.8 "The Denominator:
 Summed Area Tables"):
-* the table definition (sum of every pixel above and to the left, inclusive,
-  as the naiveRow / naiveCol listings scan) -> brute-force definition on tiny
-  images and numpy's cumulative sums (a library routine the oracle does not
-  use);
-* the four-corner box equation and satBox listing -> every rectangle of tiny
+* the table definition (sum of every pixel above and to the left, inclusive;
+  the oracle fills it by the 2-D inclusion-exclusion recurrence) ->
+  brute-force definition on tiny images and numpy's cumulative sums (a
+  library routine the oracle does not use);
+* the four-corner box identity (Figure 15-7) -> every rectangle of tiny
   images against direct slice sums;
 * the width analysis (int64 table, uint32 row running sums) -> the closed
   forms of an all-255 image.
