@@ -4,11 +4,11 @@
 // What is computed is the per-window accumulation of The CUDA Handbook
 // ch. 15 "Image in shared memory" (SumI, SumISq, SumIT over a wT x hT
 // template, then the coefficient).  SumIT and SumI are accumulated per
-// window, as that listing does, on the matrix cores; SumISq is read off
-// running column sums of the strip's row window sums of I^2 (the four-corner
-// rule of section 15.8 on the strip's own summed-area table of I^2, the
-// horizontal difference taken first).  Every sum is an exact integer, so the
-// route does not change a single output bit.
+// window, as that section does, on the matrix cores; the sum of squares is
+// read off running column sums of the strip's row window sums of squares
+// (the four-corner rule of section 15.8 on the strip's own summed-area table,
+// the horizontal difference taken first).  Every sum is an exact integer, so
+// the route does not change a single output bit.
 //
 // SumIT as a matrix product.  For template row j and the 16 positions
 // x0 + 16n + m (m = 0..15) of one 16-column block n, row j contributes
@@ -19,11 +19,14 @@
 //   A[m][(j,u)] = T[j][u - m],  B[(j,u)][n] = I[y + j][x0 + 16n + u],
 // K = 16 rows x 32 = 512 k-slots, 8 steps of v_mfma_i32_16x16x64_i8 per 256
 // positions of one output row; half of A is structural zeros.  The
-// instruction multiplies signed bytes, so both sides move by 128 (T' = T^0x80
-// inside the band, 0 outside it; I' = I^0x80) and C = sum over the window of
-// I'T', from which
-//   num = K*SumIT - SumI*SumT = K*C + SumI*(128K - SumT) + 128K*SumT - 16384K^2
-// exactly (24-bit multiplies modulo 2^32; |num| < 2^31).
+// instruction multiplies signed bytes, so both sides move by 128 (T' = T - 128
+// inside the band, 0 outside it; I' = I - 128, the byte I^0x80 read as signed)
+// and C = sum over the window of I'T'.  Numerator and variance do not change
+// when every pixel or every template byte moves by the same amount, so with
+// D = sum of I' over the window, sT = sum of T' and V = sum of I'^2
+//   num  = K*SumIT - SumI*SumT = K*C - D*sT,
+//   varI = K*SumISq - SumI^2  = K*V - D^2
+// exactly (24-bit multiplies modulo 2^32; |num|, varI < 2^31).
 //
 // Operand layout (16x16x64, as the bank kernel uses it): lane 16g + m of A
 // holds 16 k-slots of row m, lane 16g + n of B the same 16 k-slots of column
@@ -34,17 +37,20 @@
 // rows per lane, one new 16-byte read per output row.  Its results are the
 // four adjacent positions x0 + 16n + 4g .. +3.
 //
-// Window sums.  SumI is the same product with an all-ones template, whose
-// band matrix does not depend on the template row: one constant A operand, a
-// second chain of 8 steps on the same B operands.  SumISq: the lane's row
-// sums of I^2 at its 4 positions (dot4 for the first, then the squares that
+// Window sums.  D is the same product with an all-ones template, whose band
+// matrix does not depend on the template row: one constant A operand, a
+// second chain of 8 steps on the same B operands.  V: the lane's row sums of
+// I'^2 at its 4 positions (signed dot4 for the first, then the squares that
 // enter and leave as the window slides 1 byte), added down a ring of the
-// last 16 rows.
+// last 16 rows.  The plain sums, when asked for, follow from these:
+// SumI = D + 128K, SumISq = V + 256D + 16384K, SumIT = C + 128(D + sT) + 16384K.
 //
 // A workgroup (4 wavefronts, 256 columns each) owns 1024 output columns and
 // 32 output rows.  The strip's 48 image rows (rows + halo) are read once with
-// one round of 16-byte loads and staged in LDS (unsigned bytes); the loop
-// then runs without barriers.  Software pipeline: iteration y reads row y +
+// one round of 16-byte loads and staged in LDS as I^0x80: the rows the
+// first RS/4 output rows read before the loop, the rest (whose loads arrive
+// meanwhile) at output row RS/4, the loop's one barrier.  Software
+// pipeline: iteration y reads row y +
 // 1's LDS data and issues its chains, while finishing row y.  Before the
 // stores the results go through a lane permutation so that each store
 // instruction writes 1 KB of a row in lane order.
@@ -65,12 +71,6 @@ constexpr int TZ_NT = TZ_WAVES * 64;   // lanes per workgroup
 constexpr int TZ_NC = TZ_WAVES * 256;  // output columns per workgroup
 constexpr int TZ_CH = TZ_NC / 16 + 1;  // 16-byte chunks staged per row (tile + halo)
 constexpr int TZ_PITCH = TZ_CH * 4 + 4;  // dwords per LDS row
-// SumISq keeps a ring of the last 16 rows' row sums of I^2 in registers
-// (TZ_RING 1), or recomputes the leaving row's sums from LDS (0; 126
-// registers, 4 wavefronts per SIMD at 16-row strips, measured no faster)
-#ifndef TZ_RING
-#define TZ_RING 1
-#endif
 // Strip of RS output rows: RS + 16 staged image rows (the strip and its
 // halo), read with LOADS 16-byte loads per lane; BUFROWS also holds the tail
 // of the last round of loads (never read), so that every load is stored
@@ -102,36 +102,37 @@ __device__ __forceinline__ uint4 tz_load16_any(const uint8_t *img, size_t ip, in
                       align_bytes(d[3], d[2], sh), align_bytes(d[4], d[3], sh));
 }
 
-// Byte q (0..19) of the 5-dword little-endian sequence d.
+// Byte q (0..19) of the 5-dword little-endian sequence d, as a signed byte.
 template <int Q>
-__device__ __forceinline__ uint32_t byte_at(const uint32_t (&d)[5]) {
-    return (d[Q >> 2] >> (8 * (Q & 3))) & 0xffu;
+__device__ __forceinline__ int sbyte_at(const uint32_t (&d)[5]) {
+    return (int)(int8_t)(uint8_t)(d[Q >> 2] >> (8 * (Q & 3)));
 }
 
-// Row window sums of I^2 at the four columns c0 .. c0+3 whose bytes start
-// at d[0] (byte 0 = column c0): the first window by dot4, then each next one
-// by adding the square that enters and removing the one that leaves
-// (b'^2 - b^2 = (b' - b)(b' + b)).
+// Row window sums of I'^2 (signed bytes) at the four columns c0 .. c0+3
+// whose bytes start at d[0] (byte 0 = column c0): the first window by signed
+// dot4, then each next one by adding the square that enters and removing the
+// one that leaves (b'^2 - b^2 = (b' - b)(b' + b)).  Each is at most
+// 16 * 128^2.
 template <int WT>
-__device__ __forceinline__ void row_sq4(const uint32_t (&d)[5], uint32_t (&q)[4]) {
+__device__ __forceinline__ void row_sq4(const uint32_t (&d)[5], int (&q)[4]) {
     constexpr int WT4 = (WT + 3) / 4;
-    uint32_t s2 = 0;
+    int s2 = 0;
 #pragma unroll
     for (int k = 0; k < WT4; k++) {
         const uint32_t v = (k == WT4 - 1) ? (d[k] & byte_mask(WT - 4 * k)) : d[k];
-        s2 = dot4u(v, v, s2);
+        s2 = __builtin_amdgcn_sdot4((int)v, (int)v, s2, false);
     }
     q[0] = s2;
 #pragma unroll
     for (int t = 0; t < 3; t++) {
-        uint32_t bo, bn;
+        int bo, bn;
         // byte t leaves, byte t + WT enters
         switch (t) {
-            case 0: bo = byte_at<0>(d); bn = byte_at<WT>(d); break;
-            case 1: bo = byte_at<1>(d); bn = byte_at<WT + 1>(d); break;
-            default: bo = byte_at<2>(d); bn = byte_at<WT + 2>(d); break;
+            case 0: bo = sbyte_at<0>(d); bn = sbyte_at<WT>(d); break;
+            case 1: bo = sbyte_at<1>(d); bn = sbyte_at<WT + 1>(d); break;
+            default: bo = sbyte_at<2>(d); bn = sbyte_at<WT + 2>(d); break;
         }
-        q[t + 1] = q[t] + (uint32_t)__mul24((int)bn - (int)bo, (int)(bn + bo));
+        q[t + 1] = q[t] + __mul24(bn - bo, bn + bo);
     }
 }
 
@@ -148,15 +149,19 @@ __device__ __forceinline__ void to_lane_order(V (&v)[4], int pidx) {
 }
 
 // Two workgroups (8 wavefronts) per CU: up to 256 registers per lane.
-#ifndef TZ_WPE
-#define TZ_WPE (TZ_RING ? 2 : 4)
-#endif
 template <int WT, int RS, int ALIGN, bool WSUM>
-__global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t, int ntx, int nty) {
+__global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int ntx, int nty) {
     static_assert(RS % 16 == 0, "strips of whole 16-row groups");
     constexpr int NG = RS / 16;           // output-row groups of 16
     constexpr int TZ_LOADS = TzStrip<RS>::LOADS;
     constexpr int TZ_BUFROWS = TzStrip<RS>::BUFROWS;
+    // The loads are staged in two parts: the first UA (every row that rows
+    // 0 .. YB-1 read) before the loop, the rest at row YB, so that the later
+    // rows' loads arrive while the first rows are computed.  Row y reads
+    // image rows up to y + 17 (its successor's window and B operands).
+    constexpr int YB = RS / 4;
+    constexpr int UA = ((YB + 17) * TZ_CH + TZ_NT - 1) / TZ_NT;
+    static_assert(UA <= TZ_LOADS && UA * TZ_NT / TZ_CH >= YB + 17, "first part holds rows 0 .. YB+16");
     constexpr int K = WT * TZ_HT;
     __shared__ uint32_t buf[TZ_BUFROWS][TZ_PITCH];  // image rows y0 .. y0 + TZ_ROWS - 1 (+ tail)
     __shared__ uint32_t tE[TZ_HT][16];      // template row j at bytes 16 .. 16+wT-1 of 64, as T^0x80
@@ -213,12 +218,15 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
             tsum[w][1] = (int)p2;
         }
     }
-#pragma unroll
-    for (int u = 0; u < TZ_LOADS; u++) {
+    auto stage = [&](int u) {  // load u into LDS, as I^0x80
         const int i = tid + u * TZ_NT;
         const int r = i / TZ_CH, c = i % TZ_CH;
-        *(uint4 *)&buf[r][4 * c] = pre[u];
-    }
+        const uint4 v = pre[u];
+        *(uint4 *)&buf[r][4 * c] = make_uint4(v.x ^ 0x80808080u, v.y ^ 0x80808080u,
+                                              v.z ^ 0x80808080u, v.w ^ 0x80808080u);
+    };
+#pragma unroll
+    for (int u = 0; u < UA; u++) stage(u);
     __syncthreads();
 
     // ---- A operands: step s, lane (g, m = n): template row s + 8(g >> 1),
@@ -241,12 +249,12 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
     // summed over the wavefront and then over the 4 wavefronts
     const int sT1 = tsum[0][0] + tsum[1][0] + tsum[2][0] + tsum[3][0];
     const int sT2 = tsum[0][1] + tsum[1][1] + tsum[2][1] + tsum[3][1];
-    // SumT = sum T' + 128K; varT = K * sum T'^2 - (sum T')^2 (shift-invariant;
-    // <= K^2 * 127.5^2 < 2^31)
-    const int sumT = sT1 + 128 * K;
-    const float varTf = (float)((unsigned)K * (unsigned)sT2 - (unsigned)(sT1 * sT1));
-    const int ca = 128 * K - sumT;
-    const int cb = (int)((unsigned)(128 * K) * (unsigned)sumT - (unsigned)(16384 * K) * (unsigned)K);
+    // varT = K * sum T'^2 - (sum T')^2 (shift-invariant; <= K^2 * 127.5^2 < 2^31).
+    // The epilogue forms -varI (one multiply-add) and multiplies it by -varT:
+    // the same float product, since negation is exact (both are integers
+    // >= 1 unless num = 0, where the coefficient is 0 either way).
+    const float nvarTf = -(float)((unsigned)K * (unsigned)sT2 - (unsigned)(sT1 * sT1));
+    const int nsT = -sT1;
 
     // ---- lane geometry
     const int wcol = 256 * w;                      // wavefront's first column (rel. X0)
@@ -262,17 +270,16 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
     const int c0 = X0 + wcol + 4 * l;              // the lane's first position after that
     const bool wfull = X0 + wcol >= a.xs && X0 + wcol + 256 <= a.Wo;  // wave-uniform
 
-    auto bload = [&](int r) -> v4i {  // image row r (rel. y0) of the lane's B chunk, as I^0x80
+    auto bload = [&](int r) -> v4i {  // image row r (rel. y0) of the lane's B chunk (I^0x80)
         const uint4 v = *(const uint4 *)&buf[r][bch];
-        return (v4i){(int)(v.x ^ 0x80808080u), (int)(v.y ^ 0x80808080u), (int)(v.z ^ 0x80808080u),
-                     (int)(v.w ^ 0x80808080u)};
+        return (v4i){(int)v.x, (int)v.y, (int)v.z, (int)v.w};
     };
     auto hload = [&](int r, uint32_t (&d)[5]) {  // window bytes of image row r
         const uint32_t *p = &buf[r][hdw];
 #pragma unroll
         for (int k = 0; k < 5; k++) d[k] = p[k];
     };
-    auto hsq = [&](int r, uint32_t (&q)[4]) {  // row sums of I^2 of image row r
+    auto hsq = [&](int r, int (&q)[4]) {  // row sums of I'^2 of image row r
         uint32_t d[5];
         hload(r, d);
         row_sq4<WT>(d, q);
@@ -282,9 +289,10 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
     v4i bring[8];
 #pragma unroll
     for (int s = 0; s < 8; s++) bring[s] = bload(s + roff);
-    // SumI on the matrix cores too: the band matrix of an all-ones template
-    // is the same for every template row, so one A operand serves all 8
-    // steps (lane (g, m): byte i is 1 iff 0 <= 16(g & 1) + i - m < wT)
+    // D (the window sum of I') on the matrix cores too: the band matrix of
+    // an all-ones template is the same for every template row, so one A
+    // operand serves all 8 steps (lane (g, m): byte i is 1 iff
+    // 0 <= 16(g & 1) + i - m < wT)
     v4i aone;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
@@ -296,28 +304,21 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
         }
         aone[k] = (int)v;
     }
-    // ring of row sums of I^2: slot r & 15 holds image row r; SumISq of
-    // output row 0 starts as the sum over image rows 0 .. 14
-#if TZ_RING
-    uint32_t ring[4][16];
-#endif
-    uint32_t VQ[4] = {0, 0, 0, 0};
+    // ring of row sums of I'^2: slot r & 15 holds image row r; V of output
+    // row 0 starts as the sum over image rows 0 .. 14
+    int ring[4][16], VQ[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < 15; r++) {
-        uint32_t q[4];
+        int q[4];
         hsq(r, q);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-#if TZ_RING
             ring[i][r] = q[i];
-#endif
             VQ[i] += q[i];
         }
     }
-#if TZ_RING
 #pragma unroll
     for (int i = 0; i < 4; i++) ring[i][15] = 0;
-#endif
 
     // per-strip bases keep the per-lane offsets within 32 bits
     const size_t plane = a.oplane;
@@ -344,9 +345,6 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
     }
     uint32_t hd[5];  // window bytes of image row y + 15 (for row y)
     hload(15, hd);
-#if !TZ_RING
-    uint32_t ho[5] = {0, 0, 0, 0, 0};  // ... and of row y - 1 (none for row 0)
-#endif
     v4i nb = bload(8 + roff);  // step 7 of row 1
 
 #pragma unroll
@@ -354,14 +352,15 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
 #pragma unroll
         for (int yy = 0; yy < 16; yy++) {
             const int y = 16 * q + yy;
+            if (y == YB) {  // the rest of the strip (wave-uniform, all lanes)
+#pragma unroll
+                for (int u = UA; u < TZ_LOADS; u++) stage(u);
+                __syncthreads();
+            }
             // reads for row y + 1
             uint32_t hdN[5];
             v4i nbN = nb;
             if (y + 1 < RS) hload(y + 16, hdN);
-#if !TZ_RING
-            uint32_t hoN[5];
-            if (y + 1 < RS) hload(y, hoN);
-#endif
             if (y + 2 < RS) nbN = bload(y + 9 + roff);
             v4i accN = (v4i){0, 0, 0, 0}, acoN = (v4i){0, 0, 0, 0};
             if (y + 1 < RS) {
@@ -374,30 +373,16 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
                 bring[yy & 7] = nb;
             }
             nb = nbN;
-            // SumISq of row y: row y + 15 enters, row y - 1 leaves
-            uint32_t qq[4];
+            // V of row y: row y + 15 enters, row y - 1 leaves
+            int qq[4];
             row_sq4<WT>(hd, qq);
 #pragma unroll
             for (int k = 0; k < 5; k++) hd[k] = hdN[k];
-#if TZ_RING
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 VQ[i] += qq[i] - ring[i][(yy + 15) & 15];
                 ring[i][(yy + 15) & 15] = qq[i];
             }
-#else
-            if (y > 0) {
-                uint32_t qo[4];
-                row_sq4<WT>(ho, qo);
-#pragma unroll
-                for (int i = 0; i < 4; i++) VQ[i] += qq[i] - qo[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; i++) VQ[i] += qq[i];
-            }
-#pragma unroll
-            for (int k = 0; k < 5; k++) ho[k] = hoN[k];
-#endif
             const v4i acc = accC, aco = acoC;
             accC = accN;
             acoC = acoN;
@@ -409,13 +394,15 @@ __global__ __launch_bounds__(TZ_NT, TZ_WPE) void corr_toeplitz(CorrArgs a, int t
             int sI[4], sQ[4], sIT[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int sumI = aco[i] + 128 * K;  // the ones chain sums I^0x80
-                const int num = __mul24(sumI, ca) + __mul24(K, acc[i]) + cb;
-                const unsigned varI = __umul24((unsigned)K, VQ[i]) - (unsigned)__mul24(sumI, sumI);
-                gv[i] = ncc_coef((float)num, (float)varI, varTf);
-                sI[i] = sumI;
-                sQ[i] = (int)VQ[i];
-                sIT[i] = acc[i] + 128 * (sumI + sumT) - 16384 * K;
+                const int D = aco[i], C = acc[i];  // sums of I' and of I'T' over the window
+                const int num = (int)((unsigned)__mul24(D, nsT) + (unsigned)__mul24(K, C));
+                const int nvarI = __mul24(D, D) - __mul24(K, VQ[i]);
+                gv[i] = ncc_coef((float)num, (float)nvarI, nvarTf);
+                if (WSUM) {
+                    sI[i] = D + 128 * K;
+                    sQ[i] = VQ[i] + 256 * D + 16384 * K;
+                    sIT[i] = C + 128 * (D + sT1) + 16384 * K;
+                }
             }
             to_lane_order(gv, pidx);
             if (WSUM) {
