@@ -598,9 +598,11 @@ def main():
         out["large_template_workload"] = lt_out
 
         # the 1024 x 1024 smooth-noise image with its 32 x 32 template: the
-        # vector-unit tile kernel the library picks (window sums from the
-        # staged tile), against the dot4 roof of its MACs, and the generic
-        # kernel (table build + window sums from the tables) on the same call
+        # matrix-core tile kernel the library picks (one int8 16x16x64
+        # product per template row on 16 x 16 output tiles; window sums on
+        # the vector units from the staged tile), against the int8 matrix
+        # and HBM roofs; the vector-unit tile kernel (against the dot4 roof
+        # of the same MACs) and the generic kernel on the same call
         mw = synth.make("medium")
         mi = torch.from_numpy(mw["img"]).to(d)
         mt = torch.from_numpy(np.ascontiguousarray(mw["tpl"])).to(d)
@@ -615,16 +617,29 @@ def main():
 
         ramp([medium], 0.03)
         t_m, = time_each([medium], 50, stream)
+        with ncc.options(route="tile"):
+            t_mt, = time_each([medium], 20, stream)
         with ncc.options(route="generic"):
             t_mg, = time_each([medium], 10, stream)
         mmacs = mHo * mWo * mhT * mwT
+        # issued int8 ops: per 256 outputs one 16x16x64 product (32768 ops)
+        # per template row, rounded up to 8 rows
+        m_issued = (mHo * mWo / 256.0) * ((mhT + 7) // 8 * 8) * 32768
+        m_bytes = mH * mW + 4 * mHo * mWo
         out["medium_workload"] = {
             "workload": "1024x1024 u8 smooth noise, one 32x32 template cut with +-8 noise: ncc_correlate",
             "us": round(t_m * 1e3, 2), "Gcoeff/s": round(mHo * mWo / (t_m * 1e-3) / 1e9, 1),
+            "kernels": "corr_mtile<32> (int8 matrix cores, 16x16 output tiles; window sums on the "
+                       "vector units from the staged tile)",
             "useful_TOP/s": round(2 * mmacs / (t_m * 1e-3) / 1e12, 2),
-            "frac_dot4_roof": round(2 * mmacs / (t_m * 1e-3) / 1e12 / DOT4_PEAK_TOPS, 4),
-            "dot4_roof_us": round(2 * mmacs / (DOT4_PEAK_TOPS * 1e12) * 1e6, 2),
-            "kernels": "corr_tile<8> (vector units, window sums from the LDS tile)",
+            "frac_mfma_useful": round(2 * mmacs / (t_m * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
+            "frac_mfma_issued": round(m_issued / (t_m * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
+            "frac_hbm": round(m_bytes / (t_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofs_us": {"hbm": round(m_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+                         "int8_mfma_issued": round(m_issued / (INT8_MFMA_PEAK_TOPS * 1e12) * 1e6, 2),
+                         "dot4_same_macs": round(2 * mmacs / (DOT4_PEAK_TOPS * 1e12) * 1e6, 2)},
+            "frac_dot4_roof_same_macs": round(2 * mmacs / (t_m * 1e-3) / 1e12 / DOT4_PEAK_TOPS, 4),
+            "vector_tile_route_us": round(t_mt * 1e3, 2),
             "generic_route_us": round(t_mg * 1e3, 2)}
 
     if not args.no_cpu_baseline:

@@ -28,7 +28,7 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
-SOURCES = ["sat.hip", "tpl.hip", "corr.hip", "toeplitz.hip", "tile.hip", "bank.hip", "fft.hip", "ncc_api.hip"]
+SOURCES = ["sat.hip", "tpl.hip", "corr.hip", "toeplitz.hip", "mtile.hip", "tile.hip", "bank.hip", "fft.hip", "ncc_api.hip"]
 PEAKS_SOURCES = ["peaks.hip"]
 
 

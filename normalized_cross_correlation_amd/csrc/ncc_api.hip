@@ -255,10 +255,13 @@ int correlate_request(const Request &r, hipStream_t st) {
                          (route == NCC_ROUTE_SINGLE || corr_toeplitz_preferred(r.w, r.h));
     const bool stream_ok = toep_ok || ((single_route || route == NCC_ROUTE_DOT4) &&
                                        corr_stream_supported(wT, hT));
-    // the tile kernel: templates up to 32 x 64 that no kernel above takes
-    const bool tile_ok = !bank && !stream_ok && (autor || route == NCC_ROUTE_TILE) &&
+    // templates up to 32 x 32 that no kernel above takes: the matrix-core
+    // tile kernel; then the vector-unit tile kernel (up to 32 x 64, or
+    // forced by NCC_ROUTE_TILE)
+    const bool mtile_ok = !bank && !stream_ok && single_route && corr_mtile_supported(wT, hT);
+    const bool tile_ok = !bank && !stream_ok && !mtile_ok && (autor || route == NCC_ROUTE_TILE) &&
                          corr_tile_supported(wT, hT);
-    const bool need_tables = !bank && !stream_ok && !tile_ok;  // the generic and FFT routes
+    const bool need_tables = !bank && !stream_ok && !mtile_ok && !tile_ok;  // the generic and FFT routes
     if (need_tables && !corr_generic_supported(wT, hT)) return NCC_EUNSUPPORTED;
     const bool fft = need_tables && fft_chosen(route, r.w + wT - 1, r.h + hT - 1, r.w, r.h, wT,
                                                hT, nTpl);
@@ -295,11 +298,12 @@ int correlate_request(const Request &r, hipStream_t st) {
     a.coef = r.coef;
 
     // the streaming and tile kernels derive everything from the caller's buffers
-    if (!bank && (stream_ok || tile_ok)) {
+    if (!bank && (stream_ok || mtile_ok || tile_ok)) {
         for (int t = 0; t < nTpl; t++) {
-            hipError_t e = tile_ok  ? corr_tile_launch(a, t, st)
-                           : toep_ok ? corr_toeplitz_launch(a, t, st)
-                                     : corr_stream_launch(a, t, st);
+            hipError_t e = tile_ok    ? corr_tile_launch(a, t, st)
+                           : mtile_ok ? corr_mtile_launch(a, t, st)
+                           : toep_ok  ? corr_toeplitz_launch(a, t, st)
+                                      : corr_stream_launch(a, t, st);
             if (e != hipSuccess) return hip_status(e);
         }
         return NCC_OK;

@@ -118,6 +118,12 @@ struct CorrArgs {
 bool corr_stream_supported(int wT, int hT);
 hipError_t corr_stream_launch(const CorrArgs &a, int t, hipStream_t st);
 
+// Single template up to 32 x 32 on the int8 matrix cores in 16 x 16 output
+// tiles (one banded product per template row; window sums from running
+// column sums of the tile's row sums).
+bool corr_mtile_supported(int wT, int hT);
+hipError_t corr_mtile_launch(const CorrArgs &a, int t, hipStream_t st);
+
 // Single template on the int8 matrix cores (SumIT as a banded Toeplitz
 // product; window sums from the strip's running column sums).
 bool corr_toeplitz_supported(int wT, int hT);
@@ -250,6 +256,25 @@ NCC_DEV uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t s) {
 // Mask keeping the low nb bytes of a dword (nb in 1..4).
 NCC_DEV uint32_t byte_mask(int nb) {
     return nb >= 4 ? 0xffffffffu : ((1u << (8 * nb)) - 1u);
+}
+
+// Bytes x .. x+15 of row y (row y at img + y * ip) for images without
+// 16-byte aligned rows: five aligned dwords, byte-aligned.  Each dword
+// address is clamped to the dword holding the row's last byte, so every read
+// touches an image byte (an aligned dword never straddles a page).  Bytes
+// past the last row or column are then arbitrary: they feed only positions
+// past Ho or Wo, which are not stored.
+NCC_DEV uint4 load16_any(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
+    const uint8_t *row = img + (size_t)min(y, H - 1) * ip;
+    const uint8_t *first = row + min(x, W - 1), *lastb = row + W - 1;
+    const uint32_t sh = (uint32_t)((uintptr_t)first & 3);
+    const uint32_t *base = (const uint32_t *)(first - sh);
+    const uint32_t *last = (const uint32_t *)(lastb - ((uintptr_t)lastb & 3));
+    uint32_t d[5];
+#pragma unroll
+    for (int k = 0; k < 5; k++) d[k] = *(base + k <= last ? base + k : last);
+    return make_uint4(align_bytes(d[1], d[0], sh), align_bytes(d[2], d[1], sh),
+                      align_bytes(d[3], d[2], sh), align_bytes(d[4], d[3], sh));
 }
 
 // The coefficient from exact integer numerator and window variance and the

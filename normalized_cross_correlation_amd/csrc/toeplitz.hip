@@ -83,25 +83,6 @@ struct TzStrip {
     static constexpr int BUFROWS = (LOADS * TZ_NT + TZ_CH - 1) / TZ_CH;
 };
 
-// Bytes x .. x+15 of row y (row y at img + y * ip) for images without
-// 16-byte aligned rows: five aligned dwords, byte-aligned.  Each dword
-// address is clamped to the dword holding the row's last byte, so every read
-// touches an image byte (an aligned dword never straddles a page).  Bytes
-// past the last row or column are then arbitrary: they feed only positions
-// past Ho or Wo, which are not stored.
-__device__ __forceinline__ uint4 tz_load16_any(const uint8_t *img, size_t ip, int W, int H, int x, int y) {
-    const uint8_t *row = img + (size_t)min(y, H - 1) * ip;
-    const uint8_t *first = row + min(x, W - 1), *lastb = row + W - 1;
-    const uint32_t sh = (uint32_t)((uintptr_t)first & 3);
-    const uint32_t *base = (const uint32_t *)(first - sh);
-    const uint32_t *last = (const uint32_t *)(lastb - ((uintptr_t)lastb & 3));
-    uint32_t d[5];
-#pragma unroll
-    for (int k = 0; k < 5; k++) d[k] = *(base + k <= last ? base + k : last);
-    return make_uint4(align_bytes(d[1], d[0], sh), align_bytes(d[2], d[1], sh),
-                      align_bytes(d[3], d[2], sh), align_bytes(d[4], d[3], sh));
-}
-
 // Byte q (0..19) of the 5-dword little-endian sequence d, as a signed byte.
 template <int Q>
 __device__ __forceinline__ int sbyte_at(const uint32_t (&d)[5]) {
@@ -197,7 +178,7 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
             // or Wo, which are not stored, so what they hold is immaterial.
             pre[u] = *(const uint4 *)(a.img + (size_t)min(y, a.H - 1) * a.ip + min(x, a.W - 16));
         } else {
-            pre[u] = tz_load16_any(a.img, a.ip, a.W, a.H, x, y);
+            pre[u] = load16_any(a.img, a.ip, a.W, a.H, x, y);
         }
     }
     // template rows with a 16-byte zero margin on both sides, as signed

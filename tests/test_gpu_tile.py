@@ -54,11 +54,11 @@ def test_tile_shapes(oracle_mod, H, W, hT, wT, seed, want_sums):
 
 def test_tile_medium_config(oracle_mod):
     """The 1024 x 1024 smooth-noise image with its 32 x 32 template cut with
-    +-8 noise, on the default route (which takes the tile kernel), in full."""
+    +-8 noise, on the tile kernel, in full."""
     d = need_gpu()
     announce("tile medium 1024x1024 32x32")
     w = synth.make("medium")
-    _check(oracle_mod, w["img"], w["tpl"], d, name=None)
+    _check(oracle_mod, w["img"], w["tpl"], d)
 
 
 def test_tile_several_templates(oracle_mod):
