@@ -59,6 +59,7 @@ constexpr int MT_ROWS = 64;            // staged image rows (MT_NR + MT_HMAX - 1
 constexpr int MT_CH = 8;               // staged 16-byte chunks per row (128 bytes)
 constexpr int MT_PITCH = MT_CH * 4 + 4;  // dwords per staged row (+16 bytes against bank conflicts)
 constexpr int MT_TPITCH = 24;          // dwords per template row: 16 zero bytes, the row, zeros
+constexpr int MT_CSP = 36;             // dwords per row of running sums: [g][8] + 16 bytes (banks)
 constexpr int DPP_ROW_SHARE15 = 0x15f;  // every lane of a 16-lane row reads its lane 15
 
 // Row window sums of I' (r) and I'^2 (q), signed bytes, at the four columns
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(MT_NT, 2) void corr_mtile(CorrArgs a, int t, int nt
     constexpr int RR = (MT_NR + NJ - 1 + 15) / 16;
     __shared__ uint32_t img_s[MT_ROWS][MT_PITCH];      // image rows Y0 .. Y0+63 as I^0x80
     __shared__ uint32_t tpl_s[NJ][MT_TPITCH];          // template row j at bytes 16 .. 16+wT-1, as T^0x80
-    __shared__ int cs_s[MT_WAVES][MT_ROWS][4][8];      // running column sums (per wavefront)
+    __shared__ int cs_s[MT_WAVES][MT_ROWS][MT_CSP];     // running column sums (per wavefront)
     __shared__ int tsum[MT_WAVES][2];
 
     const int tix = xcd_tile((int)blockIdx.x, ntx * nty);
@@ -125,18 +126,35 @@ __global__ __launch_bounds__(MT_NT, 2) void corr_mtile(CorrArgs a, int t, int nt
     }
     // ---- template rows with 16-byte zero margins, as signed bytes (rows
     // past hT are zero, so their matrix-core steps add nothing), and the
-    // sums of T' and T'^2
+    // sums of T' and T'^2.  Every byte is read from a clamped in-bounds index
+    // and masked afterwards (no branch), so all of a lane's loads issue
+    // together.
     const uint8_t *T = a.tpl + (size_t)t * hT * wT;
+    constexpr int TE = NJ * MT_TPITCH;              // staged template dwords
+    constexpr int TIT = (TE + MT_NT - 1) / MT_NT;   // per lane
+    uint32_t tbyte[TIT][4];
+#pragma unroll
+    for (int it = 0; it < TIT; it++) {
+        const int e = tid + it * MT_NT, j = e / MT_TPITCH, dw = e % MT_TPITCH;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int c = 4 * dw + b - 16;
+            const bool ok = e < TE && j < hT && c >= 0 && c < wT;
+            tbyte[it][b] = T[ok ? j * wT + c : 0];
+        }
+    }
     int st1 = 0, st2 = 0;
-    for (int e = tid; e < NJ * MT_TPITCH; e += MT_NT) {
-        const int j = e / MT_TPITCH, dw = e % MT_TPITCH;
+#pragma unroll
+    for (int it = 0; it < TIT; it++) {
+        const int e = tid + it * MT_NT, j = e / MT_TPITCH, dw = e % MT_TPITCH;
         uint32_t v = 0;
 #pragma unroll
         for (int b = 0; b < 4; b++) {
             const int c = 4 * dw + b - 16;
-            if (j < hT && c >= 0 && c < wT) v |= ((uint32_t)T[j * wT + c] ^ 0x80u) << (8 * b);
+            const bool ok = e < TE && j < hT && c >= 0 && c < wT;
+            v |= ok ? (tbyte[it][b] ^ 0x80u) << (8 * b) : 0u;
         }
-        tpl_s[j][dw] = v;
+        if (e < TE) tpl_s[j][dw] = v;
         st1 = __builtin_amdgcn_sdot4((int)v, 0x01010101, st1, false);
         st2 = __builtin_amdgcn_sdot4((int)v, (int)v, st2, false);
     }
@@ -177,21 +195,21 @@ __global__ __launch_bounds__(MT_NT, 2) void corr_mtile(CorrArgs a, int t, int nt
     const float varTf = (float)((long long)K * sT2 - (long long)sT1 * sT1);
 
     // ---- SumIT: two 16 x 16 tiles (output rows Y0 + n and Y0 + 16 + n),
-    // one step per template row; lane (g, n) reads image rows n + j and
-    // 16 + n + j, bytes 16w + 16g .. +15
+    // one step per template row.  Lane (g, n) reads image row n + s (bytes
+    // 16w + 16g .. +15) once for both tiles: template row s of the first,
+    // row s - 16 of the second.
     v4i acc0 = (v4i){0, 0, 0, 0}, acc1 = (v4i){0, 0, 0, 0};
     const int bcol = 4 * w + 4 * g;
 #pragma unroll
-    for (int j = 0; j < NJ; j++) {
-        const v4i b0 = *(const v4i *)&img_s[n + j][bcol];
-        const v4i b1 = *(const v4i *)&img_s[16 + n + j][bcol];
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b1, acc1, 0, 0, 0);
+    for (int s = 0; s < NJ + 16; s++) {
+        const v4i b = *(const v4i *)&img_s[n + s][bcol];
+        if (s < NJ) acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s], b, acc0, 0, 0, 0);
+        if (s >= 16) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s - 16], b, acc1, 0, 0, 0);
     }
 
     // ---- window sums: row sums of image rows 16 rho + n over the windows of
     // positions 16w + 4g .. +3, running sums down the rows (with the carry of
-    // the earlier rounds), into cs_s[w][row][g][r0..r3, q0..q3]
+    // the earlier rounds), into cs_s[w][row][8g .. 8g+7] = r0..r3, q0..q3
     uint32_t mk[8];
 #pragma unroll
     for (int k = 0; k < 8; k++) mk[k] = byte_mask(min(max(wT - 4 * k, 0), 4));
@@ -215,8 +233,8 @@ __global__ __launch_bounds__(MT_NT, 2) void corr_mtile(CorrArgs a, int t, int nt
             v[k] = row16_scan(v[k]) + carry[k];
             carry[k] = __builtin_amdgcn_update_dpp(0, v[k], DPP_ROW_SHARE15, 0xf, 0xf, false);
         }
-        *(int4 *)&cs_s[w][r][g][0] = make_int4(v[0], v[1], v[2], v[3]);
-        *(int4 *)&cs_s[w][r][g][4] = make_int4(v[4], v[5], v[6], v[7]);
+        *(int4 *)&cs_s[w][r][8 * g] = make_int4(v[0], v[1], v[2], v[3]);
+        *(int4 *)&cs_s[w][r][8 * g + 4] = make_int4(v[4], v[5], v[6], v[7]);
     }
     // (cs_s rows are written and then read by the same wavefront: LDS keeps
     // a wavefront's accesses in order)
@@ -235,8 +253,8 @@ __global__ __launch_bounds__(MT_NT, 2) void corr_mtile(CorrArgs a, int t, int nt
         int lo[8], hi[8];
         {
             const int rl = max(o - 1, 0), rh = o + hT - 1;
-            const int4 l0 = *(const int4 *)&cs_s[w][rl][g][0], l1 = *(const int4 *)&cs_s[w][rl][g][4];
-            const int4 h0 = *(const int4 *)&cs_s[w][rh][g][0], h1 = *(const int4 *)&cs_s[w][rh][g][4];
+            const int4 l0 = *(const int4 *)&cs_s[w][rl][8 * g], l1 = *(const int4 *)&cs_s[w][rl][8 * g + 4];
+            const int4 h0 = *(const int4 *)&cs_s[w][rh][8 * g], h1 = *(const int4 *)&cs_s[w][rh][8 * g + 4];
             const int z = o > 0 ? 1 : 0;  // the running sum above row 0 is 0
             lo[0] = z * l0.x; lo[1] = z * l0.y; lo[2] = z * l0.z; lo[3] = z * l0.w;
             lo[4] = z * l1.x; lo[5] = z * l1.y; lo[6] = z * l1.z; lo[7] = z * l1.w;
