@@ -556,7 +556,9 @@ def main():
         # place, dense output): a local search around the template's origin
         # and a large sub-image, both at offsets that are not 16-byte aligned
         (cx, cy), = w["cut_xy"]
-        rect_out = {"workload": "4096x4096 headline image, 16x16 template: ncc_correlate_rect"}
+        rect_out = {"workload": "4096x4096 headline image, 16x16 template: ncc_correlate_rect",
+                    "kernels": "corr_mtile<16> (matrix-core tiles) below 128 strip workgroups, "
+                               "corr_toeplitz<16,16> (matrix-core strips) above"}
         for name, rw, rh in RECTS:
             x0, y0 = rect_origin((cx, cy), rw, rh, Wo, Ho)
             rcoef = torch.empty((1, rh, rw), dtype=torch.float32, device=d)

@@ -163,9 +163,10 @@ int ncc_box(const int64_t *S, int W, int H, const int32_t *rects, int64_t n,
  * (nTpl > 1) of templates with at most 16 rows of at most 16 pixels runs
  * SumIT as an int8 matrix-core contraction; one template of 16 rows and 13
  * to 16 columns runs on the int8 matrix cores as a banded Toeplitz product
- * (small launches on the vector units); other templates up to 32 x 32 run
- * on the int8 matrix cores in 16 x 16 output tiles (one banded product per
- * template row), those up to 32 x 64 on the vector units; larger ones run
+ * streamed down image strips; other templates up to 32 x 32, and 16-row
+ * ones in small launches (under about 1.5 M positions), run on the int8
+ * matrix cores in 16 x 16 output tiles (one banded product per template
+ * row), those up to 32 x 64 on the vector units; larger ones run
  * the generic kernel or, where estimated
  * faster (about 48 x 48 and up on a 4096 x 4096 image), a product of 2-D
  * Fourier transforms in double precision rounded to the integer SumIT it
@@ -251,13 +252,15 @@ int ncc_correlate_rect(const uint8_t *img, int W, int H, size_t img_pitch,
  *                         images up to 8192 x 8192 padded), NCC_ROUTE_SINGLE
  *                         (one template at a time; the matrix-core kernels
  *                         wherever the shape fits), NCC_ROUTE_DOT4 (the
- *                         vector-unit streaming kernel), NCC_ROUTE_TILE (the
+ *                         vector-unit streaming kernel for 16-row templates
+ *                         13 to 16 wide), NCC_ROUTE_TILE (the
  *                         vector-unit tile kernel).  A forced route runs
  *                         every template on its own (no bank kernel); where
  *                         its kernel does not take the shape, the generic
- *                         kernel runs (NCC_ROUTE_SINGLE first tries the
- *                         streaming kernel, then the matrix-core tile
- *                         kernel).
+ *                         kernel runs (NCC_ROUTE_SINGLE takes the
+ *                         matrix-core strip kernel for 16-row templates 13
+ *                         to 16 wide at any launch size, else the
+ *                         matrix-core tile kernel).
  *   NCC_OPT_SAT_BUILD     NCC_SAT_TWO_PASS (default) or NCC_SAT_SINGLE_PASS.
  *   NCC_OPT_TZ_STRIP      rows per workgroup of the matrix-core single-
  *                         template kernel: 0 (default: chosen per launch),

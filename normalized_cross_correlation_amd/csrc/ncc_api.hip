@@ -247,14 +247,14 @@ int correlate_request(const Request &r, hipStream_t st) {
     const int route = opt_get(NCC_OPT_CORR_ROUTE);
     const bool autor = route == NCC_ROUTE_AUTO;
     const bool bank = autor && corr_bank_supported(wT, hT, nTpl);
-    // single-template kernels: the matrix-core one, else the dot4 stream
+    // single-template kernels: the matrix-core strip kernel for 16-row
+    // templates (small launches, e.g. a local search, take the matrix-core
+    // tile kernel below; NCC_ROUTE_SINGLE forces the strip kernel where it
+    // applies); the vector-unit stream only when forced (NCC_ROUTE_DOT4)
     const bool single_route = autor || route == NCC_ROUTE_SINGLE;
-    // (small launches, e.g. a local search, take the vector-unit kernel;
-    // NCC_ROUTE_SINGLE forces the matrix-core one where it applies)
     const bool toep_ok = single_route && corr_toeplitz_supported(wT, hT) &&
                          (route == NCC_ROUTE_SINGLE || corr_toeplitz_preferred(r.w, r.h));
-    const bool stream_ok = toep_ok || ((single_route || route == NCC_ROUTE_DOT4) &&
-                                       corr_stream_supported(wT, hT));
+    const bool stream_ok = toep_ok || (route == NCC_ROUTE_DOT4 && corr_stream_supported(wT, hT));
     // templates up to 32 x 32 that no kernel above takes: the matrix-core
     // tile kernel; then the vector-unit tile kernel (up to 32 x 64, or
     // forced by NCC_ROUTE_TILE)

@@ -475,11 +475,13 @@ hipError_t launch_tz_w(const CorrArgs &a, int t, hipStream_t st) {
 
 bool corr_toeplitz_supported(int wT, int hT) { return hT == 16 && wT >= 13 && wT <= 16; }
 
-// A launch of fewer than 64 workgroups (1024 columns x 16 rows each) is
-// latency-bound, and there the vector-unit kernel's narrower workgroups are
-// faster (256 x 256 positions: 7.5 us against 10.6 us).
+// A launch of fewer than 128 workgroups (1024 columns x 16 rows each) is
+// latency-bound, and there the matrix-core tile kernel's 64 x 32 workgroups
+// are faster (search rectangles on a 4096 x 4096 image, 16 x 16 template:
+// 1024 x 1024 positions 8.0 against 10.9 us; 1536 x 1536 14.4 against
+// 11.3 us).
 bool corr_toeplitz_preferred(int Wo, int Ho) {
-    return (long long)((Wo + TZ_NC - 1) / TZ_NC) * ((Ho + 15) / 16) >= 64;
+    return (long long)((Wo + TZ_NC - 1) / TZ_NC) * ((Ho + 15) / 16) >= 128;
 }
 
 hipError_t corr_toeplitz_launch(const CorrArgs &a, int t, hipStream_t st) {
