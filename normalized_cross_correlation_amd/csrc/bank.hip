@@ -20,9 +20,13 @@
 // is a 16-byte piece of one template row (row c / NB16, bytes 16*(c % NB16)).
 //
 // A workgroup (4 wavefronts) owns 64 x 16 output positions and NB (1 or 2) blocks of
-// 16 templates.  It stages the image tile + halo in LDS as int8, then
+// 16 templates.  It stages the image tile + halo in LDS as int8 (all of its
+// 16-byte loads in flight at once), then
 //   1. window statistics: SumI and 1/sqrt(varI) of its 1024 positions (row
-//      window sums per image row, then the hT-row sums), kept in LDS;
+//      window sums per image row, each 4-column item by one dot4 window and
+//      three 1-byte slides, then the hT-row sums), kept in LDS; every step
+//      issues its LDS loads together, so the phase costs a few LDS round
+//      trips rather than one per dword;
 //   2. per row of 64 positions (4 groups of 16 A rows): byte-aligns the
 //      chunks, runs KSTEPS x 4 MFMAs per block of 16 templates, turns each
 //      result into a coefficient with the statistics of its position and
@@ -30,6 +34,8 @@
 //      that each store instruction covers 256 contiguous bytes of each of 4
 //      template maps (the MFMA result layout spreads one instruction over 16
 //      maps, 64 bytes each, which the memory system serves poorly).
+#include <algorithm>
+
 #include "ncc_internal.h"
 
 namespace ncc {
@@ -44,6 +50,22 @@ constexpr int BX = 64;  // positions per workgroup row
 constexpr int BY = 16;  // rows per workgroup
 constexpr int MAXR = BY + 15;  // tile rows for hT <= 16
 constexpr int OBP = BX + 4;    // row pitch (floats) of the output transpose buffer
+// 16-byte staging loads per thread: at most (BY + hT - 1) x (BX + 16 * nb16 +
+// 4 rounded to 16) / 16 chunks over hT * nb16 <= 16 (the largest: hT = 1,
+// wT = 256: 16 rows x 21 chunks)
+constexpr int STAGE_LOADS = 2;
+// row window sum items (4 columns each) per thread: at most MAXR x BX / 4
+constexpr int ROW_ITEMS = (MAXR * (BX / 4) + 255) / 256;
+// one LDS array for the row window sums of I' and I'^2 (MAXR x BX each) and,
+// later, the per-wavefront transpose buffers (4 x 16 templates x OBP)
+constexpr int UBUF = 2 * MAXR * BX > 4 * 16 * OBP ? 2 * MAXR * BX : 4 * 16 * OBP;
+// LDS of one workgroup, static part (UBUF, SumI and 1/sqrt(varI) per position)
+constexpr int STATIC_LDS = 4 * UBUF + 2 * 4 * BY * BX;
+// Two workgroups per CU at most (the LDS request of each is raised to more
+// than a third of the CU's 160 KB): more in flight spread the output writes
+// over more DRAM pages at once and slow the whole bank down (64 templates at
+// 4096^2: 1.50 against 1.06 ms with three per CU).
+constexpr int LDS_TWO_PER_CU = 56 * 1024;
 
 __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
@@ -52,12 +74,14 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
 template <int KSTEPS, int NB, bool FULLT>
 __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch, int rowsT,
                                                  int g0, int ntx, int nty, int nz) {
-    extern __shared__ uint32_t tile[];  // rowsT x pitch bytes of I' = I ^ 0x80
-    __shared__ int hsI[MAXR][BX];       // row window sums of I'
-    __shared__ int hsQ[MAXR][BX];       // row window sums of I'^2
+    extern __shared__ __align__(16) uint32_t tile[];  // rowsT x pitch bytes of I' = I ^ 0x80
+    // The row window sums (step 1) and the output transpose buffers (step 2)
+    // are never live together: one array holds both.
+    __shared__ __align__(16) int ubuf[UBUF];
+    int(*const hsI)[BX] = (int(*)[BX])ubuf;               // row window sums of I'
+    int(*const hsQ)[BX] = (int(*)[BX])(ubuf + MAXR * BX);  // row window sums of I'^2
     __shared__ int sIs[BY][BX];         // SumI per position
     __shared__ float rIs[BY][BX];       // 1/sqrt(varI) per position, 0 if varI == 0
-    __shared__ float obuf[4][16][OBP];  // per wavefront: 16 templates x 64 positions
     // Launch order: template blocks slowest, so that at any time the whole
     // chip writes the maps of one block (fewer maps in flight: 1.22 against
     // 1.39 ms for 64 maps at 4096^2); inside a block, XCD-contiguous tile
@@ -71,27 +95,25 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
     const int g = l >> 4, m = l & 15;
     const int x0 = (bxy % ntx) * BX, y0 = (bxy / ntx) * BY;
     const int pw = pitch / 4;
+    const bool a16 = ((((uintptr_t)a.img) | a.ip | (size_t)a.W) & 15) == 0;
     const int K = a.wT * a.hT;
     const int wt4 = (a.wT + 3) / 4;
 
-    // ---- stage the tile + halo as int8 (bytes outside the image are 0 ^ 0x80)
-    for (int i = tid; i < rowsT * pw; i += 256) {
-        const int r = i / pw, c = i % pw;
-        const int y = y0 + r, xb = x0 + 4 * c;
-        uint32_t v = 0;
-        if (y < a.H) {
-            const uint8_t *row = a.img + (size_t)y * a.ip;
-            if (xb + 3 < a.W && ((((uintptr_t)row + xb) & 3) == 0)) {
-                v = *(const uint32_t *)(row + xb);
-            } else {
+    // ---- stage the tile + halo as int8, 16 bytes per load, every load issued
+    // before the first is used.  A 16-byte aligned image (address and row
+    // pitch) takes clamped in-bounds addresses; bytes of columns past W or
+    // rows past H then repeat image bytes, and those feed only positions
+    // past Wo or Ho or meet zero template bytes (the padding of the B
+    // operands), so what they hold is immaterial.
+    const int pc = pitch / 16, nch = rowsT * pc;  // 16-byte chunks
+    uint4 pre[STAGE_LOADS];
 #pragma unroll
-                for (int b = 0; b < 4; b++)
-                    if (xb + b < a.W) v |= (uint32_t)row[xb + b] << (8 * b);
-            }
-        }
-        tile[i] = v ^ 0x80808080u;
+    for (int u = 0; u < STAGE_LOADS; u++) {
+        const int i = min(tid + 256 * u, nch - 1);
+        const int y = y0 + i / pc, x = x0 + 16 * (i % pc);
+        pre[u] = a16 ? *(const uint4 *)(a.img + (size_t)min(y, a.H - 1) * a.ip + min(x, a.W - 16))
+                     : load16_any(a.img, a.ip, a.W, a.H, x, y);
     }
-
     // ---- B operands and per-template constants of the NB blocks
     v4i bop[NB][KSTEPS];
     int ca[NB], cb[NB];
@@ -114,53 +136,110 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
             rT[nb] = 0.0f;
         }
     }
+#pragma unroll
+    for (int u = 0; u < STAGE_LOADS; u++) {
+        const int i = tid + 256 * u;
+        if (i < nch) {
+            const uint4 v = pre[u];
+            *(uint4 *)&tile[(i / pc) * pw + 4 * (i % pc)] =
+                make_uint4(v.x ^ 0x80808080u, v.y ^ 0x80808080u, v.z ^ 0x80808080u, v.w ^ 0x80808080u);
+        }
+    }
     __syncthreads();
 
     // ---- 1. window statistics of the tile's positions
-    // row window sums: (image row r, column c) pairs, 4 per thread pass
+    // row window sums: item (image row r, columns c0 .. c0+3).  The window at
+    // c0 by dot4 over its dwords (the bytes past wT masked off), then each
+    // next one by the byte that enters and the one that leaves:
+    // s1 += b' - b, s2 += b'^2 - b^2 = (b' - b)(b' + b).
     const int rowsHs = BY + a.hT - 1;
     const uint32_t mlast = byte_mask(a.wT - 4 * (wt4 - 1));
-    for (int i = tid; i < rowsHs * BX; i += 256) {
-        const int r = i / BX, c = i % BX;
-        const uint32_t *p = tile + r * pw + (c >> 2);
-        const uint32_t sh = (uint32_t)(c & 3);
+    const int8_t *tb = (const int8_t *)tile;
+    const int nit = rowsHs * (BX / 4);
+    // masks of a window's first four dwords: whole, the last one's wT bytes, none
+    uint32_t mk[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) mk[k] = k < wt4 - 1 ? 0xffffffffu : k == wt4 - 1 ? mlast : 0u;
+#pragma unroll
+    for (int it = 0; it < ROW_ITEMS; it++) {
+        // an index past the last item repeats it (loads in bounds, no store)
+        const int i = min(tid + 256 * it, nit - 1);
+        const int r = i / (BX / 4), c0 = 4 * (i % (BX / 4));
+        const uint32_t *p = tile + r * pw + (c0 >> 2);
+        const int8_t *pn = tb + r * pitch + c0 + a.wT;  // bytes entering
+        uint32_t d[4];
+        int bn[3];
+#pragma unroll
+        for (int k = 0; k < 4; k++) d[k] = p[k];
+#pragma unroll
+        for (int t = 0; t < 3; t++) bn[t] = pn[t];
         int s1 = 0, s2 = 0;
-        uint32_t lo = p[0];
-        for (int k = 0; k < wt4; k++) {
-            const uint32_t hi = p[k + 1];
-            uint32_t v = align_bytes(hi, lo, sh);
-            // padding bytes must count as I' = 0, not as pixels
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t v = d[k] & mk[k];
+            s1 = sdot4(v, 0x01010101u, s1);
+            s2 = sdot4(v, v, s2);
+        }
+        for (int k = 4; k < wt4; k++) {  // templates wider than 16
+            uint32_t v = p[k];
             if (k == wt4 - 1) v &= mlast;
             s1 = sdot4(v, 0x01010101u, s1);
             s2 = sdot4(v, v, s2);
-            lo = hi;
         }
-        hsI[r][c] = s1;
-        hsQ[r][c] = s2;
+        int o1[4], o2[4];
+        o1[0] = s1;
+        o2[0] = s2;
+#pragma unroll
+        for (int t = 0; t < 3; t++) {
+            const int bo = (int)(int8_t)(uint8_t)(d[0] >> (8 * t));
+            s1 += bn[t] - bo;
+            s2 += __mul24(bn[t] - bo, bn[t] + bo);
+            o1[t + 1] = s1;
+            o2[t + 1] = s2;
+        }
+        if (tid + 256 * it < nit) {
+            *(int4 *)&hsI[r][c0] = make_int4(o1[0], o1[1], o1[2], o1[3]);
+            *(int4 *)&hsQ[r][c0] = make_int4(o2[0], o2[1], o2[2], o2[3]);
+        }
     }
     __syncthreads();
     {
-        // thread (c, rq): output rows 4rq .. 4rq+3 of column c
-        const int c = tid & 63, rq = tid >> 6;
-        int s1 = 0, s2 = 0;
-        for (int j = 0; j < a.hT; j++) {
-            s1 += hsI[4 * rq + j][c];
-            s2 += hsQ[4 * rq + j][c];
+        // thread (c, q): output rows r0 = RPT * q .. r0 + RPT - 1 of column c
+        constexpr int RPT = BY / 4;
+        const int c = tid & 63, r0 = RPT * (tid >> 6);
+        // rows r0 .. r0 + 15 (those past hT - 1 masked off) and the rows
+        // entering for outputs r0 + 1 .. r0 + RPT - 1, loaded together
+        int vI[16], vQ[16], eI[RPT], eQ[RPT];
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            vI[j] = hsI[r0 + j][c];
+            vQ[j] = hsQ[r0 + j][c];
         }
 #pragma unroll
-        for (int o = 0; o < 4; o++) {
+        for (int o = 1; o < RPT; o++) {
+            eI[o] = hsI[r0 + o + a.hT - 1][c];
+            eQ[o] = hsQ[r0 + o + a.hT - 1][c];
+        }
+        int s1 = 0, s2 = 0;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            s1 += j < a.hT ? vI[j] : 0;
+            s2 += j < a.hT ? vQ[j] : 0;
+        }
+#pragma unroll
+        for (int o = 0; o < RPT; o++) {
             if (o > 0) {
-                s1 += hsI[4 * rq + o + a.hT - 1][c] - hsI[4 * rq + o - 1][c];
-                s2 += hsQ[4 * rq + o + a.hT - 1][c] - hsQ[4 * rq + o - 1][c];
+                s1 += eI[o] - vI[o - 1];
+                s2 += eQ[o] - vQ[o - 1];
             }
             // SumI = sum I' + 128K;  SumISq = sum I'^2 + 256 sum I' + 16384K
             const int sumI = s1 + 128 * K;
             const int sumISq = s2 + 256 * s1 + 16384 * K;
             const unsigned varI = (unsigned)K * (unsigned)sumISq - (unsigned)sumI * (unsigned)sumI;
-            sIs[4 * rq + o][c] = sumI;
-            rIs[4 * rq + o][c] = varI ? __builtin_amdgcn_rsqf((float)varI) : 0.0f;
+            sIs[r0 + o][c] = sumI;
+            rIs[r0 + o][c] = varI ? __builtin_amdgcn_rsqf((float)varI) : 0.0f;
             if (a.sums && bz == 0 && g0 == 0) {
-                const int y = y0 + 4 * rq + o, x = x0 + c;
+                const int y = y0 + r0 + o, x = x0 + c;
                 if (y < a.Ho && x < a.Wo) {
                     const size_t plane = a.oplane, oo = (size_t)y * a.op + x;
                     __builtin_nontemporal_store(sumI, a.sums + oo);
@@ -175,7 +254,7 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
     // (4 groups of 16, the A rows) and, per block of 16 templates, turns the
     // MFMA results into coefficients, transposes them through its LDS buffer
     // and writes 256 contiguous bytes per template row.
-    float *ob = &obuf[w][0][0];
+    float *ob = (float *)ubuf + w * 16 * OBP;
     const size_t plane = a.oplane;
     const bool whole = x0 + BX <= a.Wo;  // every column of the tile is an output
     for (int yy = w; yy < BY; yy += 4) {
@@ -294,9 +373,10 @@ template <int KS>
 hipError_t launch_bank_ks(const CorrArgs &a, int nb16, int pitch, int rowsT, size_t lds,
                           hipStream_t st) {
     // groups of 16 templates: blocks of 2 groups (32 templates) per workgroup,
-    // then a last single group.  Measured at 4096^2 with 64 templates: 2
-    // groups per workgroup 1.22 ms, 4 groups 1.39 ms, 1 group 1.34 ms (each
-    // workgroup stages its tile and window statistics once per block).
+    // then a last single group.  Measured at 4096^2 with 64 templates (an
+    // earlier form of the kernel): 2 groups per workgroup 1.22 ms, 4 groups
+    // 1.39 ms, 1 group 1.34 ms (each workgroup stages its tile and window
+    // statistics once per block).
     const int ng = (a.nTpl + 15) / 16;
     const bool tail16 = (a.nTpl % 16) != 0;
     const int n2 = ng / 2, rest = ng % 2;
@@ -323,7 +403,10 @@ hipError_t corr_bank_launch(const CorrArgs &a, hipStream_t st) {
     const int ks = (a.hT * nb16 + 3) / 4;
     int pitch, rowsT;
     bank_geometry(a.wT, a.hT, &pitch, &rowsT);
-    const size_t lds = (size_t)pitch * rowsT;
+    // the tile, or more so that at most two workgroups share a CU
+    const size_t lds = std::max((size_t)pitch * rowsT, (size_t)(LDS_TWO_PER_CU - STATIC_LDS));
+    // the kernel's staging covers at most 256 * STAGE_LOADS chunks of 16 bytes
+    if (rowsT * (pitch / 16) > 256 * STAGE_LOADS) return hipErrorNotSupported;
     switch (ks) {
         case 1: return launch_bank_ks<1>(a, nb16, pitch, rowsT, lds, st);
         case 2: return launch_bank_ks<2>(a, nb16, pitch, rowsT, lds, st);
