@@ -106,13 +106,21 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
     // past Wo or Ho or meet zero template bytes (the padding of the B
     // operands), so what they hold is immaterial.
     const int pc = pitch / 16, nch = rowsT * pc;  // 16-byte chunks
+    // each chunk with the 4 bytes after it, for the byte-shifted copies
     uint4 pre[STAGE_LOADS];
+    uint32_t nxt[STAGE_LOADS];
 #pragma unroll
     for (int u = 0; u < STAGE_LOADS; u++) {
         const int i = min(tid + 256 * u, nch - 1);
         const int y = y0 + i / pc, x = x0 + 16 * (i % pc);
-        pre[u] = a16 ? *(const uint4 *)(a.img + (size_t)min(y, a.H - 1) * a.ip + min(x, a.W - 16))
-                     : load16_any(a.img, a.ip, a.W, a.H, x, y);
+        if (a16) {
+            const uint8_t *row = a.img + (size_t)min(y, a.H - 1) * a.ip;
+            pre[u] = *(const uint4 *)(row + min(x, a.W - 16));
+            nxt[u] = *(const uint32_t *)(row + min(x + 16, a.W - 4));
+        } else {
+            pre[u] = load16_any(a.img, a.ip, a.W, a.H, x, y);
+            nxt[u] = load16_any(a.img, a.ip, a.W, a.H, x + 16, y).x;
+        }
     }
     // ---- B operands and per-template constants of the NB blocks
     v4i bop[NB][KSTEPS];
@@ -136,13 +144,24 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
             rT[nb] = 0.0f;
         }
     }
+    // copy s (0..3) of the tile holds each row shifted left by s bytes, so
+    // that a 16-byte piece at any byte offset is 4 dword-aligned words of one
+    // copy
+    const int csz = rowsT * pw;  // dwords per copy
 #pragma unroll
     for (int u = 0; u < STAGE_LOADS; u++) {
         const int i = tid + 256 * u;
         if (i < nch) {
             const uint4 v = pre[u];
-            *(uint4 *)&tile[(i / pc) * pw + 4 * (i % pc)] =
-                make_uint4(v.x ^ 0x80808080u, v.y ^ 0x80808080u, v.z ^ 0x80808080u, v.w ^ 0x80808080u);
+            const uint32_t d[5] = {v.x ^ 0x80808080u, v.y ^ 0x80808080u, v.z ^ 0x80808080u,
+                                   v.w ^ 0x80808080u, nxt[u] ^ 0x80808080u};
+            uint32_t *dst = &tile[(i / pc) * pw + 4 * (i % pc)];
+            *(uint4 *)dst = make_uint4(d[0], d[1], d[2], d[3]);
+#pragma unroll
+            for (int sh = 1; sh < 4; sh++)
+                *(uint4 *)(dst + sh * csz) =
+                    make_uint4(align_bytes(d[1], d[0], sh), align_bytes(d[2], d[1], sh),
+                               align_bytes(d[3], d[2], sh), align_bytes(d[4], d[3], sh));
         }
     }
     __syncthreads();
@@ -260,7 +279,9 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
     for (int yy = w; yy < BY; yy += 4) {
         const int y = y0 + yy;
         if (y >= a.Ho) break;
-        // A operands: group mg, row m = position 16*mg + m, chunk c = 4*ks + g
+        // A operands: group mg, row m = position 16*mg + m, chunk c = 4*ks + g;
+        // the piece starts at byte offset off, off % 4 = m % 4 (pitch is a
+        // multiple of 16), read from the copy shifted by m % 4
         v4i A[4][KSTEPS];
 #pragma unroll
         for (int mg = 0; mg < 4; mg++)
@@ -269,11 +290,8 @@ __global__ __launch_bounds__(256) void corr_bank(CorrArgs a, int nb16, int pitch
                 const int c = 4 * ks + g, j = c / nb16, ib = c % nb16;
                 const int jj = j < a.hT ? j : 0;  // padding chunks meet zero template bytes
                 const int off = (yy + jj) * pitch + 16 * mg + m + 16 * ib;
-                const uint32_t *p = tile + (off >> 2);
-                const uint32_t sh = (uint32_t)(off & 3);
-                const uint32_t d0 = p[0], d1 = p[1], d2 = p[2], d3 = p[3], d4 = p[4];
-                A[mg][ks] = (v4i){(int)align_bytes(d1, d0, sh), (int)align_bytes(d2, d1, sh),
-                                  (int)align_bytes(d3, d2, sh), (int)align_bytes(d4, d3, sh)};
+                const uint32_t *p = tile + (m & 3) * csz + (off >> 2);
+                A[mg][ks] = (v4i){(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
             }
         // statistics of this lane's result rows: positions 16*mg + 4g .. +3
         int4 sI4[4];
@@ -403,8 +421,8 @@ hipError_t corr_bank_launch(const CorrArgs &a, hipStream_t st) {
     const int ks = (a.hT * nb16 + 3) / 4;
     int pitch, rowsT;
     bank_geometry(a.wT, a.hT, &pitch, &rowsT);
-    // the tile, or more so that at most two workgroups share a CU
-    const size_t lds = std::max((size_t)pitch * rowsT, (size_t)(LDS_TWO_PER_CU - STATIC_LDS));
+    // the tile's four copies, or more so that at most two workgroups share a CU
+    const size_t lds = std::max((size_t)4 * pitch * rowsT, (size_t)(LDS_TWO_PER_CU - STATIC_LDS));
     // the kernel's staging covers at most 256 * STAGE_LOADS chunks of 16 bytes
     if (rowsT * (pitch / 16) > 256 * STAGE_LOADS) return hipErrorNotSupported;
     switch (ks) {
