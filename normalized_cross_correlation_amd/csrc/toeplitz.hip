@@ -285,9 +285,18 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
         }
         aone[k] = (int)v;
     }
-    // ring of row sums of I'^2: slot r & 15 holds image row r; V of output
-    // row 0 starts as the sum over image rows 0 .. 14
-    int ring[4][16], VQ[4] = {0, 0, 0, 0};
+    // The same band, negated on lane groups 0 and 1 (bytes 0xff = -1), for
+    // the window sum's slide from row to row: with B from one ring slot
+    // (image row r on groups 0, 1 and row r + 8 on groups 2, 3) one step adds
+    // rs(r + 8) - rs(r), rs = the row window sums of I'.
+    v4i adiff;
+#pragma unroll
+    for (int k = 0; k < 4; k++) adiff[k] = g < 2 ? (int)((uint32_t)aone[k] * 0xffu) : aone[k];
+    // ring of row sums of I'^2: slot r & 15 holds image row r.  The running
+    // value is NV = -K * V (V the window's sum of I'^2), so that -varI =
+    // D^2 + NV is one multiply-add; output row 0 starts from image rows
+    // 0 .. 14 (|NV| <= K^2 * 128^2 <= 2^30).
+    int ring[4][16], NV[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < 15; r++) {
         int q[4];
@@ -295,23 +304,25 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             ring[i][r] = q[i];
-            VQ[i] += q[i];
+            NV[i] -= K * q[i];
         }
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) ring[i][15] = 0;
 
-    // per-strip bases keep the per-lane offsets within 32 bits
     const size_t plane = a.oplane;
     float *outp = a.coef + (size_t)t * plane + (size_t)y0 * a.op;
     int32_t *sp0 = WSUM ? a.sums + (size_t)y0 * a.op : nullptr;
     int32_t *sp1 = WSUM ? sp0 + plane : nullptr;
     int32_t *sp2 = WSUM ? a.sums + (size_t)(2 + t) * plane + (size_t)y0 * a.op : nullptr;
-    // Offsets are signed: a view may start left of its first output (xs > 0),
-    // so the first wavefront's row base lies before the row's first output.
-    // Within a strip they stay below RS * op < 2^31 (op < 2^24).
-    const int op = (int)a.op;
-    int orow = c0 - a.xs;          // the lane's first output of the next row
+    // The lane's pointers to its output of column c0 in the next row (xs is
+    // the column of a view's first output), advanced by op each row: one
+    // 64-bit add per row and plane.
+    const size_t op = a.op;
+    float *orp = outp + (c0 - a.xs);
+    int32_t *s0p = WSUM ? sp0 + (c0 - a.xs) : nullptr;
+    int32_t *s1p = WSUM ? sp1 + (c0 - a.xs) : nullptr;
+    int32_t *s2p = WSUM ? sp2 + (c0 - a.xs) : nullptr;
 
     // Software pipeline: iteration y reads from LDS what row y + 1 needs,
     // issues the matrix-core chain of row y + 1 and finishes row y (window
@@ -343,14 +354,17 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
             v4i nbN = nb;
             if (y + 1 < RS) hload(y + 16, hdN);
             if (y + 2 < RS) nbN = bload(y + 9 + roff);
-            v4i accN = (v4i){0, 0, 0, 0}, acoN = (v4i){0, 0, 0, 0};
+            v4i accN = (v4i){0, 0, 0, 0}, acoN = acoC;
             if (y + 1 < RS) {
 #pragma unroll
                 for (int s = 0; s < 8; s++) {
                     const v4i b = s < 7 ? bring[(yy + 1 + s) & 7] : nb;
                     accN = __builtin_amdgcn_mfma_i32_16x16x64_i8(atp[s], b, accN, 0, 0, 0);
-                    acoN = __builtin_amdgcn_mfma_i32_16x16x64_i8(aone, b, acoN, 0, 0, 0);
                 }
+                // D(y + 1) = D(y) + rs(y + 16) - rs(y): slot y & 7 holds rows
+                // y, y + 8 (groups 0, 1 / 2, 3), nb rows y + 8, y + 16
+                acoN = __builtin_amdgcn_mfma_i32_16x16x64_i8(adiff, bring[yy & 7], acoN, 0, 0, 0);
+                acoN = __builtin_amdgcn_mfma_i32_16x16x64_i8(adiff, nb, acoN, 0, 0, 0);
                 bring[yy & 7] = nb;
             }
             nb = nbN;
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
             for (int k = 0; k < 5; k++) hd[k] = hdN[k];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                VQ[i] += qq[i] - ring[i][(yy + 15) & 15];
+                NV[i] += __mul24(ring[i][(yy + 15) & 15] - qq[i], K);
                 ring[i][(yy + 15) & 15] = qq[i];
             }
             const v4i acc = accC, aco = acoC;
@@ -377,11 +391,11 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
             for (int i = 0; i < 4; i++) {
                 const int D = aco[i], C = acc[i];  // sums of I' and of I'T' over the window
                 const int num = (int)((unsigned)__mul24(D, nsT) + (unsigned)__mul24(K, C));
-                const int nvarI = __mul24(D, D) - __mul24(K, VQ[i]);
+                const int nvarI = __mul24(D, D) + NV[i];
                 gv[i] = ncc_coef((float)num, (float)nvarI, nvarTf);
                 if (WSUM) {
                     sI[i] = D + 128 * K;
-                    sQ[i] = VQ[i] + 256 * D + 16384 * K;
+                    sQ[i] = -NV[i] / K + 256 * D + 16384 * K;
                     sIT[i] = C + 128 * (D + sT1) + 16384 * K;
                 }
             }
@@ -393,35 +407,40 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
             }
             if (y < rowsOut) {  // wave-uniform
                 if (wfull) {
-                    __builtin_nontemporal_store((f4u){gv[0], gv[1], gv[2], gv[3]}, (f4u *)(outp + orow));
+                    __builtin_nontemporal_store((f4u){gv[0], gv[1], gv[2], gv[3]}, (f4u *)orp);
                     if (WSUM) {
                         if (t == 0) {
                             __builtin_nontemporal_store((i4u){sI[0], sI[1], sI[2], sI[3]},
-                                                        (i4u *)(sp0 + orow));
+                                                        (i4u *)s0p);
                             __builtin_nontemporal_store((i4u){sQ[0], sQ[1], sQ[2], sQ[3]},
-                                                        (i4u *)(sp1 + orow));
+                                                        (i4u *)s1p);
                         }
                         __builtin_nontemporal_store((i4u){sIT[0], sIT[1], sIT[2], sIT[3]},
-                                                    (i4u *)(sp2 + orow));
+                                                    (i4u *)s2p);
                     }
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         const int x = c0 + i;
                         if (x >= a.xs && x < a.Wo) {
-                            outp[orow + i] = gv[i];
+                            orp[i] = gv[i];
                             if (WSUM) {
                                 if (t == 0) {
-                                    sp0[orow + i] = sI[i];
-                                    sp1[orow + i] = sQ[i];
+                                    s0p[i] = sI[i];
+                                    s1p[i] = sQ[i];
                                 }
-                                sp2[orow + i] = sIT[i];
+                                s2p[i] = sIT[i];
                             }
                         }
                     }
                 }
             }
-            orow += op;
+            orp += op;
+            if (WSUM) {
+                s0p += op;
+                s1p += op;
+                s2p += op;
+            }
             // keep each iteration's loads and arithmetic inside it
             __builtin_amdgcn_sched_barrier(0);
         }
