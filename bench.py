@@ -391,10 +391,11 @@ def main():
 
     sat_bytes = H * W * 17  # read u8 once, write two int64 tables once
     corr_ops = coeffs * hT * wT * 2  # u8 multiply-accumulates, 2 ops each
-    # the matrix-core kernel issues 16 v_mfma_i32_16x16x64_i8 (16*16*64*2 ops
-    # each) per 256 positions -- 8 for SumIT, 8 for SumI: 2048 int8 ops per
-    # coefficient, half of them on the bands' structural zeros
-    corr_mfma_ops = coeffs * 2048
+    # the matrix-core kernel issues 10 v_mfma_i32_16x16x64_i8 (16*16*64*2 ops
+    # each) per 256 positions -- 8 for SumIT (half of them on the band's
+    # structural zeros), 2 sliding SumI from the row above: 1280 int8 ops per
+    # coefficient (the first row of each 32-row strip takes 8 more for SumI)
+    corr_mfma_ops = coeffs * 1280
     corr_bytes = H * W + coeffs * 4  # image read once, coefficients written once
     sat_rate = sat_bytes / (t_sat * 1e-3) / 1e9
     corr_gbs = corr_bytes / (t_corr * 1e-3) / 1e9

@@ -139,8 +139,9 @@ __device__ __forceinline__ void tile_sums(const uint8_t *__restrict__ img, int W
     uint32_t(*red)[16][SAT_SW] = (uint32_t(*)[16][SAT_SW])lds;  // [table][row-group pair][column]
     uint32_t *btw = lds + 2 * 16 * SAT_SW;                        // [wave] half-tile totals
     // dword k of the 4 rows, transposed so that word c holds column 4k+c of
-    // rows 0..3; then lanes l and l^8 (row groups 2j, 2j+1) add
-    uint32_t ci[16], cq[16];
+    // rows 0..3; then lanes l and l^8 (row groups 2j, 2j+1) add, and the
+    // even row group writes the 4 columns (one dword group at a time, so few
+    // sums are live at once)
 #pragma unroll
     for (int k = 0; k < 4; k++) {
         const uint32_t d0 = ((const uint32_t *)&px[0])[k], d1 = ((const uint32_t *)&px[1])[k];
@@ -149,22 +150,17 @@ __device__ __forceinline__ void tile_sums(const uint8_t *__restrict__ img, int W
         const uint32_t e2 = perm(d3, d2, 0x06020400u), e3 = perm(d3, d2, 0x07030501u);
         const uint32_t tc[4] = {perm(e2, e0, 0x05040100u), perm(e3, e1, 0x05040100u), perm(e2, e0, 0x07060302u),
                                 perm(e3, e1, 0x07060302u)};
+        uint32_t ci[4], cq[4];
 #pragma unroll
         for (int c = 0; c < 4; c++) {
-            ci[4 * k + c] = dot4u(tc[c], 0x01010101u, 0);
-            cq[4 * k + c] = dot4u(tc[c], tc[c], 0);
+            ci[c] = dot4u(tc[c], 0x01010101u, 0);
+            cq[c] = dot4u(tc[c], tc[c], 0);
+            ci[c] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ci[c], DPP_ROW_ROR8, 0xf, 0xf, false);
+            cq[c] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cq[c], DPP_ROW_ROR8, 0xf, 0xf, false);
         }
-    }
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        ci[j] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ci[j], DPP_ROW_ROR8, 0xf, 0xf, false);
-        cq[j] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cq[j], DPP_ROW_ROR8, 0xf, 0xf, false);
-    }
-    if ((rg & 1) == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            *(uint4 *)&red[0][rg >> 1][16 * cg + 4 * k] = make_uint4(ci[4 * k], ci[4 * k + 1], ci[4 * k + 2], ci[4 * k + 3]);
-            *(uint4 *)&red[1][rg >> 1][16 * cg + 4 * k] = make_uint4(cq[4 * k], cq[4 * k + 1], cq[4 * k + 2], cq[4 * k + 3]);
+        if ((rg & 1) == 0) {
+            *(uint4 *)&red[0][rg >> 1][16 * cg + 4 * k] = make_uint4(ci[0], ci[1], ci[2], ci[3]);
+            *(uint4 *)&red[1][rg >> 1][16 * cg + 4 * k] = make_uint4(cq[0], cq[1], cq[2], cq[3]);
         }
     }
     __syncthreads();

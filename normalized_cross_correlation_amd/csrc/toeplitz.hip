@@ -38,11 +38,15 @@
 // four adjacent positions x0 + 16n + 4g .. +3.
 //
 // Window sums.  D is the same product with an all-ones template, whose band
-// matrix does not depend on the template row: one constant A operand, a
-// second chain of 8 steps on the same B operands.  V: the lane's row sums of
-// I'^2 at its 4 positions (signed dot4 for the first, then the squares that
-// enter and leave as the window slides 1 byte), added down a ring of the
-// last 16 rows.  The plain sums, when asked for, follow from these:
+// matrix does not depend on the template row: one constant A operand.  The
+// strip's first row takes the 8-step chain; each next row slides it,
+// D(y + 1) = D(y) + rs(y + 16) - rs(y) (rs = row window sums of I'), in two
+// steps whose A operand is the band negated on lane groups 0 and 1: a ring
+// slot holds rows r and r + 8 on the two halves, so one step adds
+// rs(r + 8) - rs(r).  V: the lane's row sums of I'^2 at its 4 positions
+// (signed dot4 for the first, then the squares that enter and leave as the
+// window slides 1 byte), added down a ring of the last 16 rows; the running
+// value is -K*V, so that -varI = D^2 - K*V is one multiply-add.  The plain sums, when asked for, follow from these:
 // SumI = D + 128K, SumISq = V + 256D + 16384K, SumIT = C + 128(D + sT) + 16384K.
 //
 // A workgroup (4 wavefronts, 256 columns each) owns 1024 output columns and
