@@ -136,6 +136,24 @@ def test_bank(oracle_mod, n, hT, wT, H, W, seed):
     _compare(oracle_mod, c["img"], c["tpl"], d)
 
 
+# Both staging paths of the bank kernel: widths that are multiples of 16 take
+# 16-byte loads from clamped addresses (tiles past the right and bottom edges
+# read repeated image bytes), other widths the byte-aligned loads.  Templates
+# up to 256 bytes wide (hT = 1) need two 16-byte loads per thread for the tile
+# and halo; 17 templates end in a single 16-template block.
+@pytest.mark.parametrize("n,hT,wT,H,W,seed", [
+    (5, 16, 16, 48, 160, 51), (3, 1, 256, 20, 512, 52), (4, 2, 128, 40, 256, 53),
+    (6, 8, 32, 70, 96, 54), (17, 16, 13, 35, 64, 55), (3, 1, 256, 20, 515, 56),
+    (4, 2, 128, 40, 301, 57), (2, 16, 16, 16, 16, 58),
+])
+@pytest.mark.parametrize("want_sums", [True, False])
+def test_bank_staging_paths(oracle_mod, n, hT, wT, H, W, seed, want_sums):
+    d = need_gpu()
+    announce("correlate bank staging n=%d %dx%d img %dx%d sums=%s" % (n, hT, wT, H, W, want_sums))
+    c = synth.random_case(seed, H, W, hT, wT, nTpl=n, kind="smooth" if seed % 2 else "uniform")
+    _compare(oracle_mod, c["img"], c["tpl"], d, want_sums=want_sums)
+
+
 def test_bank_equals_single_route(oracle_mod):
     """The matrix-core bank and one-template-at-a-time give identical sums."""
     import normalized_cross_correlation_amd as ncc
