@@ -466,11 +466,14 @@ hipError_t launch_tz(const CorrArgs &a, int t, hipStream_t st) {
 // Strip height: 32 rows halve the halo of 16-row strips, but a launch of
 // fewer than two 32-row workgroups per CU leaves CUs idle; then 16 rows
 // (measured: 28.7 vs 30.5 us at 4096 x 4096, 19.3 vs 16.5 us for a 2048 x
-// 2048 search rectangle).  The option NCC_OPT_TZ_STRIP = 16 or 32 fixes it
-// instead.
+// 2048 search rectangle).  With the sums planes (four output planes instead
+// of one) the call is bound by its stores, which 16-row strips drain faster:
+// 74.6 against 82.6 us at 4096 x 4096, so those calls always take 16.  The
+// option NCC_OPT_TZ_STRIP = 16 or 32 fixes it instead.
 int tz_strip(const CorrArgs &a) {
     const int v = opt_get(NCC_OPT_TZ_STRIP);
     if (v == 16 || v == 32) return v;
+    if (a.sums) return 16;
     static int cus[NCC_MAX_DEVICES];
     int dev = 0, n = 256;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < NCC_MAX_DEVICES) {
