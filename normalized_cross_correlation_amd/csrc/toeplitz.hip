@@ -381,6 +381,10 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
             for (int i = 0; i < 4; i++) {
                 NV[i] += __mul24(ring[i][(yy + 15) & 15] - qq[i], K);
                 ring[i][(yy + 15) & 15] = qq[i];
+                // keep NV itself as the loop's running value (the compiler
+                // would otherwise carry the sum of the differences and form
+                // K times it anew for every use: one more instruction)
+                asm volatile("" : "+v"(NV[i]));
             }
             const v4i acc = accC, aco = acoC;
             accC = accN;
