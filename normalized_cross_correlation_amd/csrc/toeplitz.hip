@@ -151,6 +151,12 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
     __shared__ uint32_t buf[TZ_BUFROWS][TZ_PITCH];  // image rows y0 .. y0 + TZ_ROWS - 1 (+ tail)
     __shared__ uint32_t tE[TZ_HT][16];      // template row j at bytes 16 .. 16+wT-1 of 64, as T^0x80
     __shared__ int tsum[TZ_WAVES][2];       // per wavefront: sums of T' and T'^2
+    // Coefficient rows on their way out (no sums planes): slot [r][c][18g + n]
+    // holds, for row r of a group of 4, wavefront c's lane (g, n) results
+    // (positions 16n + 4g .. +3 of its 256 columns).  18, not 16, slots per
+    // lane group keep both the writes and the transposed reads free of bank
+    // conflicts.
+    __shared__ float4 obuf[WSUM ? 1 : 4][TZ_WAVES][72];
 
     const int tix = xcd_tile((int)blockIdx.x, ntx * nty);
     if (tix < 0) return;
@@ -327,6 +333,16 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
     int32_t *s0p = WSUM ? sp0 + (c0 - a.xs) : nullptr;
     int32_t *s1p = WSUM ? sp1 + (c0 - a.xs) : nullptr;
     int32_t *s2p = WSUM ? sp2 + (c0 - a.xs) : nullptr;
+    // Without the sums planes a group of 4 rows is written through obuf:
+    // wavefront w stores row 4k + w of the group, all 1024 columns (4 KB in
+    // four 1 KB instructions), which the memory system drains faster than
+    // four wavefronts writing 1 KB of the same row each.  rrow: this lane's
+    // first output of that row (columns X0 + 4l + 256c, c = chunk).
+    float *rrow = outp + (size_t)w * op + (X0 + 4 * l - a.xs);
+    bool cfull[TZ_WAVES];
+#pragma unroll
+    for (int c = 0; c < TZ_WAVES; c++)
+        cfull[c] = X0 + 256 * c >= a.xs && X0 + 256 * c + 256 <= a.Wo;  // wave-uniform
 
     // Software pipeline: iteration y reads from LDS what row y + 1 needs,
     // issues the matrix-core chain of row y + 1 and finishes row y (window
@@ -407,47 +423,77 @@ __global__ __launch_bounds__(TZ_NT, 2) void corr_toeplitz(CorrArgs a, int t, int
                     sIT[i] = C + 128 * (D + sT1) + 16384 * K;
                 }
             }
-            to_lane_order(gv, pidx);
-            if (WSUM) {
-                to_lane_order(sI, pidx);
-                to_lane_order(sQ, pidx);
-                to_lane_order(sIT, pidx);
-            }
-            if (y < rowsOut) {  // wave-uniform
-                if (wfull) {
-                    __builtin_nontemporal_store((f4u){gv[0], gv[1], gv[2], gv[3]}, (f4u *)orp);
-                    if (WSUM) {
-                        if (t == 0) {
-                            __builtin_nontemporal_store((i4u){sI[0], sI[1], sI[2], sI[3]},
-                                                        (i4u *)s0p);
-                            __builtin_nontemporal_store((i4u){sQ[0], sQ[1], sQ[2], sQ[3]},
-                                                        (i4u *)s1p);
-                        }
-                        __builtin_nontemporal_store((i4u){sIT[0], sIT[1], sIT[2], sIT[3]},
-                                                    (i4u *)s2p);
-                    }
-                } else {
+            if constexpr (!WSUM) {
+                obuf[yy & 3][w][18 * g + n] = make_float4(gv[0], gv[1], gv[2], gv[3]);
+                if ((yy & 3) == 3) {  // the group's 4 rows are in obuf
+                    __syncthreads();
+                    const int R = y - 3 + w;  // the row this wavefront stores
+                    float4 v[TZ_WAVES];
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int x = c0 + i;
-                        if (x >= a.xs && x < a.Wo) {
-                            orp[i] = gv[i];
-                            if (WSUM) {
-                                if (t == 0) {
-                                    s0p[i] = sI[i];
-                                    s1p[i] = sQ[i];
+                    for (int c = 0; c < TZ_WAVES; c++) v[c] = obuf[w][c][18 * (l & 3) + (l >> 2)];
+                    if (R < rowsOut) {  // wave-uniform
+#pragma unroll
+                        for (int c = 0; c < TZ_WAVES; c++) {
+                            float *dst = rrow + 256 * c;
+                            if (cfull[c]) {
+                                __builtin_nontemporal_store((f4u){v[c].x, v[c].y, v[c].z, v[c].w}, (f4u *)dst);
+                            } else {
+                                const float vv[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+                                for (int i = 0; i < 4; i++) {
+                                    const int x = X0 + 256 * c + 4 * l + i;
+                                    if (x >= a.xs && x < a.Wo) dst[i] = vv[i];
                                 }
-                                s2p[i] = sIT[i];
+                            }
+                        }
+                    }
+                    rrow += 4 * op;
+                    // reads done before the slots take the next group
+                    __syncthreads();
+                }
+            } else {
+                to_lane_order(gv, pidx);
+                if (WSUM) {
+                    to_lane_order(sI, pidx);
+                    to_lane_order(sQ, pidx);
+                    to_lane_order(sIT, pidx);
+                }
+                if (y < rowsOut) {  // wave-uniform
+                    if (wfull) {
+                        __builtin_nontemporal_store((f4u){gv[0], gv[1], gv[2], gv[3]}, (f4u *)orp);
+                        if (WSUM) {
+                            if (t == 0) {
+                                __builtin_nontemporal_store((i4u){sI[0], sI[1], sI[2], sI[3]},
+                                                            (i4u *)s0p);
+                                __builtin_nontemporal_store((i4u){sQ[0], sQ[1], sQ[2], sQ[3]},
+                                                            (i4u *)s1p);
+                            }
+                            __builtin_nontemporal_store((i4u){sIT[0], sIT[1], sIT[2], sIT[3]},
+                                                        (i4u *)s2p);
+                        }
+                    } else {
+    #pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int x = c0 + i;
+                            if (x >= a.xs && x < a.Wo) {
+                                orp[i] = gv[i];
+                                if (WSUM) {
+                                    if (t == 0) {
+                                        s0p[i] = sI[i];
+                                        s1p[i] = sQ[i];
+                                    }
+                                    s2p[i] = sIT[i];
+                                }
                             }
                         }
                     }
                 }
-            }
-            orp += op;
-            if (WSUM) {
-                s0p += op;
-                s1p += op;
-                s2p += op;
+                orp += op;
+                if (WSUM) {
+                    s0p += op;
+                    s1p += op;
+                    s2p += op;
+                }
             }
             // keep each iteration's loads and arithmetic inside it
             __builtin_amdgcn_sched_barrier(0);
