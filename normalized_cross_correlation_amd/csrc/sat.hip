@@ -420,19 +420,21 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
             t2b += R2b[r];
             int64_t *srow = S + (size_t)y * W + x;
             int64_t *qrow = Q + (size_t)y * W + x;
-            // ordinary (temporal) stores: on this part they sustain ~12% more
-            // write bandwidth than nontemporal ones for this row-run pattern
+            // S with ordinary stores, Q with nontemporal ones: on this part a
+            // mix of the two kinds sustains more write bandwidth than either
+            // kind alone for this row-run pattern (4096^2 build: 52.3 us all
+            // ordinary, 59.7 us all nontemporal, 50.7 us mixed)
             if (pair) {
                 *(v2l *)srow = v2l{(long long)t1a, (long long)t1b};
-                *(v2l *)qrow = v2l{(long long)t2a, (long long)t2b};
+                __builtin_nontemporal_store(v2l{(long long)t2a, (long long)t2b}, (v2l *)qrow);
             } else {
                 if (x < W) {
                     srow[0] = (int64_t)t1a;
-                    qrow[0] = (int64_t)t2a;
+                    __builtin_nontemporal_store((long long)t2a, (long long *)qrow);
                 }
                 if (x + 1 < W) {
                     srow[1] = (int64_t)t1b;
-                    qrow[1] = (int64_t)t2b;
+                    __builtin_nontemporal_store((long long)t2b, (long long *)(qrow + 1));
                 }
             }
         }
