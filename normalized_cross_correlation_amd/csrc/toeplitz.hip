@@ -46,18 +46,22 @@
 // rs(r + 8) - rs(r).  V: the lane's row sums of I'^2 at its 4 positions
 // (signed dot4 for the first, then the squares that enter and leave as the
 // window slides 1 byte), added down a ring of the last 16 rows; the running
-// value is -K*V, so that -varI = D^2 - K*V is one multiply-add.  The plain sums, when asked for, follow from these:
-// SumI = D + 128K, SumISq = V + 256D + 16384K, SumIT = C + 128(D + sT) + 16384K.
+// value is -K*V, so that -varI = D^2 - K*V is one multiply-add.  The plain
+// sums, when asked for, follow from these: SumI = D + 128K,
+// SumISq = V + 256D + 16384K, SumIT = C + 128(D + sT) + 16384K.
 //
 // A workgroup (4 wavefronts, 256 columns each) owns 1024 output columns and
-// 32 output rows.  The strip's 48 image rows (rows + halo) are read once with
-// one round of 16-byte loads and staged in LDS as I^0x80: the rows the
+// RS output rows (32; 16 for small launches and for calls that write the
+// sums planes).  The strip's RS + 16 image rows (rows + halo) are read once
+// with one round of 16-byte loads and staged in LDS as I^0x80: the rows the
 // first RS/4 output rows read before the loop, the rest (whose loads arrive
-// meanwhile) at output row RS/4, the loop's one barrier.  Software
-// pipeline: iteration y reads row y +
-// 1's LDS data and issues its chains, while finishing row y.  Before the
-// stores the results go through a lane permutation so that each store
-// instruction writes 1 KB of a row in lane order.
+// meanwhile) at output row RS/4.  Software pipeline: iteration y reads row y + 1's LDS
+// data and issues its chains, while finishing row y.  Coefficient rows go
+// out through an LDS buffer of 4 rows: after every 4th row (a barrier) each
+// wavefront stores one whole 1024-column row of the group, 4 KB in four
+// 1 KB instructions, and a second barrier frees the buffer.  With the sums
+// planes the results instead go through a lane permutation, and each
+// wavefront stores 1 KB of every row and plane.
 #include "ncc_internal.h"
 
 
