@@ -92,7 +92,7 @@ def test_generic_shapes(oracle_mod, H, W, hT, wT, seed):
 ])
 def test_generic_tall_and_wide(oracle_mod, H, W, hT, wT, seed):
     """Window sums from tables of images taller than 4096 rows and wider than
-    1024 columns (several chunks of bands in the table build's top pass)."""
+    1024 columns (many tile rows and strips in the table build)."""
     d = need_gpu()
     announce("correlate generic tall %dx%d tpl %dx%d" % (H, W, hT, wT))
     c = synth.random_case(seed, H, W, hT, wT, nTpl=1, kind="uniform")

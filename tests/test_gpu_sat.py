@@ -24,10 +24,11 @@ SHAPES = [
     # widths that are not multiples of 4, several tiles
     (1, 1), (1, 300), (300, 1), (7, 5), (63, 255), (64, 256), (65, 257),
     (130, 515), (200, 1023), (129, 1030), (333, 777),
-    # more than 128 bands of 32 rows and more than one 1024-column segment:
-    # the top pass scans each quarter of the bands in several 32-band chunks
+    # more than 32 tile rows, in counts that are not multiples of the 8 XCDs
+    # the tile rows are spread over (33, 65, 36), and tile prologues summing
+    # the column sums of many tiles above
     (4200, 1100), (8230, 1030), (4500, 2100),
-    # more row bands (68 750) and tiles than one grid dimension of 65 536
+    # more tile rows (17 188) and row groups than one grid dimension of 65 536
     (2200000, 3),
 ]
 
