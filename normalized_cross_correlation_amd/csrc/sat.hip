@@ -110,8 +110,9 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Two kinds of workgroup in one launch (tiles, and groups of 4 rows; the
-// launch gives each XCD the jobs of its tile rows, see sat_tiles):
+// Two kinds of workgroup in one launch (tiles, and groups of 4 rows; when the
+// tile rows divide evenly over the XCDs, each XCD gets the jobs of its tile
+// rows, see sat_tiles):
 //   tile (strip s, tile row g): thread (rg, cg) = (tid >> 3, tid & 7) holds
 //     rows 4rg .. 4rg+3 and columns 16cg .. 16cg+15 of the tile.  Writes the
 //     tile's column sums colsum[t][g][x] and its total btot[t][g][s].  Column
@@ -225,20 +226,28 @@ template <bool VEC>
 __global__ __launch_bounds__(256) void sat_tiles(const uint8_t *__restrict__ img, int W, int H, size_t ip,
                                                  SatWork wk) {
     __shared__ uint32_t lds[2 * 16 * SAT_SW + 4];
-    // The jobs of tile row g go to XCD g % NUM_XCD (blockIdx % NUM_XCD), the
-    // XCD whose downsweep workgroups take that tile row: per XCD first the
-    // tiles of its tile rows, then their 4-row groups (4096^2: 50.3 against
-    // 50.6 us per build with tiles and row groups spread over the XCDs).
-    const int x8 = (int)blockIdx.x % NUM_XCD, i8 = (int)blockIdx.x / NUM_XCD;
-    const int rows8 = (wk.nG + NUM_XCD - 1) / NUM_XCD;  // tile rows per XCD
-    if (i8 < rows8 * wk.nS) {  // block-uniform
-        const int g = x8 + NUM_XCD * (i8 / wk.nS);
-        if (g < wk.nG) tile_sums<VEC>(img, W, H, ip, wk, i8 % wk.nS, g, lds);
-    } else {
-        const int j = i8 - rows8 * wk.nS;
-        const int g = x8 + NUM_XCD * (j / (SAT_TR / 4));
-        const int b = g * (SAT_TR / 4) + j % (SAT_TR / 4);  // rows 4b .. 4b+3
-        if (g < wk.nG && b < (H + 3) / 4) row_prefixes<VEC>(img, W, H, ip, wk, b, lds);
+    if (wk.nG % NUM_XCD == 0) {  // uniform
+        // The jobs of tile row g go to XCD g % NUM_XCD (blockIdx % NUM_XCD),
+        // the XCD whose downsweep workgroups take that tile row: per XCD
+        // first the tiles of its tile rows, then their 4-row groups (4096^2:
+        // 50.3 against 50.6 us per build with tiles and row groups spread
+        // over the XCDs).
+        const int x8 = (int)blockIdx.x % NUM_XCD, i8 = (int)blockIdx.x / NUM_XCD;
+        const int rows8 = wk.nG / NUM_XCD;  // tile rows per XCD
+        if (i8 < rows8 * wk.nS) {  // block-uniform
+            tile_sums<VEC>(img, W, H, ip, wk, i8 % wk.nS, x8 + NUM_XCD * (i8 / wk.nS), lds);
+        } else {
+            const int j = i8 - rows8 * wk.nS;
+            const int g = x8 + NUM_XCD * (j / (SAT_TR / 4));
+            const int b = g * (SAT_TR / 4) + j % (SAT_TR / 4);  // rows 4b .. 4b+3
+            if (b < (H + 3) / 4) row_prefixes<VEC>(img, W, H, ip, wk, b, lds);
+        }
+    } else {  // blocks [0, nS*nG) are tiles, the rest 4-row groups
+        const int ntiles = wk.nS * wk.nG;
+        if ((int)blockIdx.x < ntiles)
+            tile_sums<VEC>(img, W, H, ip, wk, (int)blockIdx.x % wk.nS, (int)blockIdx.x / wk.nS, lds);
+        else
+            row_prefixes<VEC>(img, W, H, ip, wk, (int)blockIdx.x - ntiles, lds);
     }
 }
 
@@ -279,14 +288,24 @@ __global__ __launch_bounds__(256) void sat_downsweep(const uint8_t *__restrict__
                                                      SatWork wk, int64_t *__restrict__ S,
                                                      int64_t *__restrict__ Q) {
     const int nS = wk.nS, nG = wk.nG;
-    // Tile rows interleaved over the XCDs: the workgroups that go to XCD x
-    // (blockIdx % NUM_XCD) take tile rows x, x + NUM_XCD, ..., each with all
-    // its strips.  On this part that drains the tables' rows faster than each
-    // XCD taking a contiguous band of tile rows (4096^2: 50.5 against 50.8 us
-    // per build; strips per XCD instead of rows: 59.8 us).
-    const int x8 = (int)blockIdx.x % NUM_XCD, i8 = (int)blockIdx.x / NUM_XCD;
-    const int s = i8 % nS, g = x8 + NUM_XCD * (i8 / nS);
-    if (g >= nG) return;
+    // When the tile rows divide evenly over the XCDs, they are interleaved:
+    // the workgroups that go to XCD x (blockIdx % NUM_XCD) take tile rows x,
+    // x + NUM_XCD, ..., each with all its strips.  On this part that drains
+    // the tables' rows faster than each XCD taking a contiguous band of tile
+    // rows (4096^2: 50.5 against 50.8 us per build; strips per XCD instead of
+    // rows: 59.8 us).  Otherwise each XCD takes a contiguous range of tiles,
+    // which keeps the XCDs' shares equal for any shape.
+    int s, g;
+    if (nG % NUM_XCD == 0) {  // uniform
+        const int x8 = (int)blockIdx.x % NUM_XCD, i8 = (int)blockIdx.x / NUM_XCD;
+        s = i8 % nS;
+        g = x8 + NUM_XCD * (i8 / nS);
+    } else {
+        const int tix = xcd_tile((int)blockIdx.x, nS * nG);
+        if (tix < 0) return;
+        s = tix % nS;
+        g = tix / nS;
+    }
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int x = s * SAT_SW + 2 * l;
     const int ytile = g * SAT_TR;
@@ -823,15 +842,18 @@ hipError_t sat_build_launch(const uint8_t *img, int W, int H, size_t ip, int64_t
     const bool dvec = (W % 2 == 0) && (ip % 2 == 0) && (((uintptr_t)img & 1) == 0) &&
                       (((uintptr_t)S & 15) == 0) && (((uintptr_t)Q & 15) == 0);
     dim3 block(256);
-    // per XCD: its tile rows' tiles and 4-row groups
-    const unsigned blocks = (unsigned)(NUM_XCD * ((wk.nG + NUM_XCD - 1) / NUM_XCD) * (wk.nS + SAT_TR / 4));
+    // per XCD its tile rows' tiles and 4-row groups when the tile rows divide
+    // evenly over the XCDs, else every tile and then every 4-row group
+    const unsigned blocks = wk.nG % NUM_XCD == 0
+                                ? (unsigned)wk.nG * (unsigned)(wk.nS + SAT_TR / 4)
+                                : (unsigned)wk.nS * (unsigned)wk.nG + (unsigned)((H + 3) / 4);
     if (rvec)
         hipLaunchKernelGGL(sat_tiles<true>, dim3(blocks), block, 0, st, img, W, H, ip, wk);
     else
         hipLaunchKernelGGL(sat_tiles<false>, dim3(blocks), block, 0, st, img, W, H, ip, wk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(NUM_XCD * ((wk.nG + NUM_XCD - 1) / NUM_XCD) * wk.nS));
+    dim3 grid(xcd_grid(wk.nS * wk.nG));  // nS * nG when nG % NUM_XCD == 0
     if (dvec)
         hipLaunchKernelGGL(sat_downsweep<true>, grid, block, 0, st, img, W, H, ip, wk, S, Q);
     else
