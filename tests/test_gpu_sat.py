@@ -28,6 +28,11 @@ SHAPES = [
     # the tile rows are spread over (33, 65, 36), and tile prologues summing
     # the column sums of many tiles above
     (4200, 1100), (8230, 1030), (4500, 2100),
+    # tile rows that divide evenly over the 8 XCDs (interleaved placement)
+    # with ragged tails: 8 tile rows with a partial last 4-row group and a
+    # width not a multiple of 4, 16 tile rows, and 33 strips with rows wider
+    # than one 4096-column chunk of a row workgroup
+    (1021, 301), (2047, 129), (1024, 4100),
     # more tile rows (17 188) and row groups than one grid dimension of 65 536
     (2200000, 3),
 ]
